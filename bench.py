@@ -1,0 +1,233 @@
+"""Benchmark of the Q/K rotate + INT4-quantise hot path on one MI355X.
+
+A step is one rrp_rotate_quantize_qk launch over the whole 131072-token
+Llama-3.1-8B-shaped prefill batch (32 Q / 8 KV heads, head_dim 128, RoPE theta
+5e5, bf16, b = 128, group = 128, KV4 cache write): RoPE, the shared pair
+rotation by the calibrated angles, the block Hadamard, the Q store and the K
+group quantisation / nibble packing.  Inputs are resident in HBM before the
+timed region.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--hot-path-only]
+
+--hot-path-only skips the supporting passes, the decode timing and the CPU
+baseline (short runs under a profiler).  Every run also times a plain
+device-to-device copy of the Q tensor (known size: 1 GiB read + 1 GiB written)
+as the practical streaming ceiling and as the reference kernel that scales the
+profiler's FETCH_SIZE / WRITE_SIZE counters.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Q/K rotate+INT4-quantise tokens/sec and achieved HBM GB/s (% of peak), 1 GPU"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rotate_quantize_prefill128k_traffic.json")
+KERNEL_SOURCES = ["rotation_rope_pair_amd/csrc/rrp_device.hpp", "rotation_rope_pair_amd/csrc/rrp_rotate.hip",
+                  "rotation_rope_pair_amd/csrc/rrp_kernels.hpp"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, angles_np, budget_s=12.0):
+    """The CPU oracle (untuned) on a bounded prefix of the same workload."""
+    import oracle as O
+    shp = O.shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.rope_theta)
+    n = 256
+    t0 = time.perf_counter()
+    O.rotate_quantize_qk(shp, inp["q"][:n], inp["k"][:n], inp["pos"][:n], angles_np, 128, 128)
+    per_tok = (time.perf_counter() - t0) / n
+    n = int(min(w.n_tokens, max(256, budget_s / max(per_tok, 1e-9))))
+    t0 = time.perf_counter()
+    O.rotate_quantize_qk(shp, inp["q"][:n], inp["k"][:n], inp["pos"][:n], angles_np, 128, 128)
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {w.n_tokens} tokens, same inputs and angles, {dt:.1f} s"}
+
+
+def to_device_bf16(a, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def decode_latency_us(dev, stream, reps=50):
+    """Per-launch time of the 256-token Mistral-shaped decode batch (slot scatter
+    into a 256 x 32768-slot KV4 cache)."""
+    import torch
+    import rotation_rope_pair_amd as rrp
+    from rotation_rope_pair_amd import workloads as W
+    w5 = W.WORKLOADS[5]
+    inp5 = W.make_inputs(5)
+    shape5 = rrp.layer_shape(w5.n_q_heads, w5.n_kv_heads, w5.head_dim, w5.rope_theta)
+    q5, k5 = to_device_bf16(inp5["q"], dev), to_device_bf16(inp5["k"], dev)
+    pos5 = torch.from_numpy(inp5["pos"]).to(dev)
+    sm5 = torch.from_numpy(inp5["slot_mapping"]).to(dev)
+    c5, s5 = rrp.new_kv4_cache(inp5["n_slots"], w5.n_kv_heads, w5.head_dim, w5.group, dev)
+    q5o = torch.empty_like(q5)
+    a5 = torch.zeros(w5.n_pairs, dtype=torch.float32, device=dev)
+
+    def launch():
+        rrp.rotate_quantize_qk(shape5, q5, k5, pos5, support_b=128, group=w5.group, k_codes=c5, k_scales=s5,
+                               angles=a5, q_out=q5o, slot_mapping=sm5, n_slots=inp5["n_slots"])
+    for _ in range(5):
+        launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hot-path-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported here (the path shards "
+              "over tokens or heads without communication, but no multi-GPU run is part of this build)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rotation_rope_pair_amd as rrp
+    from rotation_rope_pair_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[4]
+    inp = W.make_inputs(4)
+    T, d, hq, hk, b, g = w.n_tokens, w.head_dim, w.n_q_heads, w.n_kv_heads, 128, 128
+    shape = rrp.layer_shape(hq, hk, d, w.rope_theta)
+    q, k = to_device_bf16(inp["q"], dev), to_device_bf16(inp["k"], dev)
+    pos = torch.from_numpy(inp["pos"]).to(dev)
+    q_out = torch.empty_like(q)
+    codes, scales = rrp.new_kv4_cache(T, hk, d, g, dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+
+    # Supporting pass 1: calibrate the shared angles (default estimator) on this batch.
+    moments = rrp.new_moments(d, dev)
+    angles = torch.empty(d // 2, dtype=torch.float32, device=dev)
+    rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
+    supporting = {}
+    if not args.hot_path_only:
+        moments.zero_()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
+        ev[1].record(stream)
+        # Supporting pass 2: the K-range / quantisation-error diagnostic at b = 128.
+        stats = torch.empty(8, dtype=torch.float64, device=dev)
+        rrp.quant_error_stats(shape, k, pos, support_b=b, group=g, stats_out=stats, angles=angles)
+        ev[2].record(stream)
+        rrp.quant_error_stats(shape, k, pos, support_b=b, group=g, stats_out=stats, angles=angles)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        st = stats.cpu().numpy()
+        supporting.update({"calibrate_angles_ms": ev[0].elapsed_time(ev[1]),
+                           "quant_error_stats_ms": ev[2].elapsed_time(ev[3]),
+                           "rel_quant_error_b128": float(np.sqrt(st[0] / st[1])),
+                           "mean_k_range_b128": float(st[2] / st[5])})
+    torch.cuda.synchronize()
+
+    def step():
+        rrp.rotate_quantize_qk(shape, q, k, pos, support_b=b, group=g, k_codes=codes, k_scales=scales,
+                               angles=angles, q_out=q_out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev[4].record(stream)
+    for _ in range(args.steps):
+        step()
+    ev[5].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = ev[4].elapsed_time(ev[5]) / args.steps
+
+    bytes_per_launch = w.bytes_per_token(group=g, with_slot=False) * T
+    achieved = bytes_per_launch / (ms * 1e-3) / 1e9
+
+    # Reference streaming kernel of known size: device copy of the Q tensor.
+    copy_bytes = 2 * q.numel() * q.element_size()
+    for _ in range(3):
+        q_out.copy_(q)
+    ev[6].record(stream)
+    for _ in range(10):
+        q_out.copy_(q)
+    ev[7].record(stream)
+    torch.cuda.synchronize()
+    copy_ms = ev[6].elapsed_time(ev[7]) / 10
+    copy_ref = {"kernel": "torch device-to-device copy of Q (bf16)", "bytes_read_plus_written": copy_bytes,
+                "ms": copy_ms, "GBs": copy_bytes / (copy_ms * 1e-3) / 1e9}
+    if not args.hot_path_only:
+        supporting["decode256_rotate_quantize_us"] = decode_latency_us(dev, stream)
+
+    out = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded per-channel Gaussian + outlier pairs + Student-t(3) tail; shapes only)",
+        "config": {"workload": w.name, "n_tokens": T, "n_q_heads": hq, "n_kv_heads": hk, "head_dim": d,
+                   "rope_theta": w.rope_theta, "support_b": b, "group": g, "global_batch": 1, "seq_len": T,
+                   "kv_cache": "int4 nibble-packed + fp16 group scales", "parallelism": "none (1 GPU)"},
+        "hbm_gbs": achieved,
+        "hbm_frac_of_peak": achieved / PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
+                     "algorithmic_bytes_per_launch": bytes_per_launch},
+        "copy_reference": copy_ref,
+        "supporting": supporting,
+        "wall_s_timed": t_wall,
+    }
+    if not (args.no_cpu_baseline or args.hot_path_only):
+        out["cpu_baseline"] = cpu_baseline(w, inp, angles.cpu().numpy())
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * rrp.h -- C-ABI of the MI355X (gfx950) library for the RoPE-aligned Q/K
+ * rotation and dynamic INT4 KV4 quantisation path.
+ *
+ * The method: "When Local Variance Optimality Is Not Enough: RoPE-Aligned Q/K
+ * Rotations for Dynamic 4-Bit Quantisation" (abstract and technical summary,
+ * sections "methodology", "optimisation objective", "estimator strategies",
+ * "contributions").  After RoPE, every Q and K row of a head is turned by a
+ * head-shared plane rotation inside each RoPE frequency pair (angle phi_k),
+ * then by a block Walsh-Hadamard transform of support b; each K row is then
+ * quantised to INT4 with a dynamic per-group absmax scale and written into a
+ * packed KV4 cache.  Q is rotated but not quantised (only K is quantised after
+ * the transform, estimator-strategies section).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE memory unless marked "host".  The caller owns every
+ *     buffer; nothing passed in is retained after the call returns.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL = the null stream).  The host returns as soon as the work is
+ *     enqueued; the caller synchronises before reading outputs.
+ *   - Arguments are validated on the host before anything is enqueued.  On an
+ *     error the function returns a non-zero rrp_status and enqueues nothing.
+ *     RRP_ERR_HIP reports a failed HIP runtime call (launch or stream-ordered
+ *     allocation); work enqueued before the failing call may have run.
+ *   - Tensors are dense, row-major, token-major: Q is [n_tokens][n_q_heads]
+ *     [head_dim], K is [n_tokens][n_kv_heads][head_dim], in `dtype`.
+ *   - Q, K and Q-output pointers must be 16-byte aligned (128-bit accesses).
+ *   - Supported head_dim: 64 and 128.  Others return RRP_ERR_UNSUPPORTED.
+ *   - Thread-safe: the library keeps no mutable global state.
+ */
+#ifndef RRP_H
+#define RRP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rrp_status {
+    RRP_OK = 0,
+    RRP_ERR_INVALID_ARG = 1,  /* NULL required pointer, bad size, bad enum value      */
+    RRP_ERR_MISALIGNED = 2,   /* a pointer violates its alignment requirement         */
+    RRP_ERR_UNSUPPORTED = 3,  /* valid in principle but not built (e.g. head_dim 96)  */
+    RRP_ERR_HIP = 4           /* a HIP runtime call failed                             */
+} rrp_status;
+
+typedef enum rrp_dtype { RRP_F32 = 0, RRP_BF16 = 1 } rrp_dtype;
+
+/* Estimators of the shared angle ("estimator strategies" section):
+ *   DEFAULT          pool the raw Q and K sums over heads and tokens, then centre
+ *                    (each sample counts once, so Q weighs H_q / H_kv times K);
+ *   K_ONLY           the covariance of the K samples alone;
+ *   STREAM_BALANCED  equal weight to the Q and K raw (uncentred) moments, each
+ *                    normalised by its own sample count, then centre. */
+typedef enum rrp_estimator {
+    RRP_EST_DEFAULT = 0,
+    RRP_EST_K_ONLY = 1,
+    RRP_EST_STREAM_BALANCED = 2
+} rrp_estimator;
+
+/* Which channels form RoPE frequency pair k (problem-statement section: RoPE
+ * splits a head into fixed two-dimensional frequency pairs).
+ *   HALF_SPLIT   (k, k + head_dim/2)   -- the Llama / Mistral convention
+ *   INTERLEAVED  (2k, 2k + 1) */
+typedef enum rrp_rope_layout { RRP_ROPE_HALF_SPLIT = 0, RRP_ROPE_INTERLEAVED = 1 } rrp_rope_layout;
+
+/* Shape of one attention layer (host struct).  RoPE frequency of pair k is
+ * fp32(rope_theta^(-2k/head_dim)) (rounded once from fp64); the angle at
+ * position p is the single fp32 product fp32(p) * freq_k. */
+typedef struct rrp_shape {
+    int32_t n_q_heads;   /* >= 0 */
+    int32_t n_kv_heads;  /* >= 1 */
+    int32_t head_dim;    /* 64 or 128 */
+    int32_t rope_layout; /* rrp_rope_layout */
+    double rope_theta;   /* > 0 */
+} rrp_shape;
+
+/* rrp_rotate_quantize_qk -- the hot path ("methodology" and "contributions"
+ * sections: RoPE, then the pair rotation, then the block Hadamard of support b;
+ * dynamic tokenwise group-range INT4 quantisation of K into the KV4 cache).
+ *
+ * For each token t, each Q head and each K head:
+ *   y = H_b / sqrt(b) . R_phi . RoPE_pos[t] (x)
+ *   H_b: Sylvester Hadamard on contiguous blocks of b channels, natural order.
+ * Q rows: y is written to q_out in `dtype` (bf16 round-to-nearest-even).
+ * K rows: for each group of `group` consecutive channels of y,
+ *   s32 = fp32(max|y| / 7); s_h = fp16(s32) (nearest-even, saturated at 65504);
+ *   code = clamp(round_half_even(y / s_h), -7, 7) (all 0 when s_h == 0);
+ *   byte i of the row = (code[2i] & 0xF) | (code[2i+1] & 0xF) << 4.
+ *
+ * shape         host; head counts, head_dim, RoPE theta and pair layout.
+ * dtype         RRP_F32 or RRP_BF16, for q, k and q_out.
+ * q             [n_tokens][n_q_heads][head_dim] or NULL (no Q rows processed).
+ * k             [n_tokens][n_kv_heads][head_dim], required.
+ * pos           int32[n_tokens] RoPE positions, each in [0, 2^24).
+ * angles        float[head_dim/2] pair angles phi_k (output of
+ *               rrp_calibrate_angles) or NULL for no pair rotation.
+ * support_b     1, 2, 4, ..., head_dim; 1 = no Hadamard (pairwise only).
+ * group         quantisation group size: a power of two in [2, head_dim].
+ * q_out         rotated Q, same layout as q; may equal q (in place); NULL = Q
+ *               not written.  Requires q.
+ * k_codes       uint8 [n_slots][n_kv_heads][head_dim/2], 4-byte aligned.
+ * k_scales      uint16 (fp16 bits) [n_slots][n_kv_heads][head_dim/group], 2-byte aligned.
+ * slot_mapping  int64[n_tokens]: cache slot of token t, or NULL for slot = t.
+ *               Tokens whose slot lies outside [0, n_slots) write nothing
+ *               (padding).  Two tokens with one slot: unspecified winner.
+ * n_slots       cache capacity in slots; with slot_mapping == NULL it must be
+ *               >= n_tokens.
+ * q_rot_f32     optional fp32 copy of rotated Q, [n_tokens][n_q_heads][head_dim], 16-B aligned.
+ * k_rot_f32     optional fp32 copy of rotated K, [n_tokens][n_kv_heads][head_dim], 16-B aligned.
+ * k_scale_f32   optional fp32 group scales s32 indexed by TOKEN (not slot),
+ *               [n_tokens][n_kv_heads][head_dim/group], 4-byte aligned.
+ * stream        hipStream_t or NULL.
+ * n_tokens == 0 is a no-op returning RRP_OK. */
+int rrp_rotate_quantize_qk(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
+                           const int32_t* pos, int64_t n_tokens, const float* angles,
+                           int32_t support_b, int32_t group, void* q_out, uint8_t* k_codes,
+                           uint16_t* k_scales, const int64_t* slot_mapping, int64_t n_slots,
+                           float* q_rot_f32, float* k_rot_f32, float* k_scale_f32, void* stream);
+
+/* rrp_calibrate_angles -- the calibration pass ("optimisation objective" and
+ * "estimator strategies" sections: a closed-form shared angle per pair that
+ * minimises the larger of the pair's two channel variances under a
+ * pooled-covariance, position-averaged surrogate).
+ *
+ * Accumulates, for every pair k and stream S in {Q, K}, the fp64 sums
+ * n, sum u, sum v, sum u^2, sum v^2, sum u*v of the post-RoPE pair (u, v) over
+ * all tokens and all heads of S into
+ *   moments   double[head_dim/2][2][6]  (stream 0 = Q, 1 = K)
+ * which the caller zeroes before the first batch and may keep across batches
+ * (it is the resumable calibration state).  Tokens are reduced in a fixed order:
+ * repeated calls on the same inputs give bit-identical moments.
+ * If angles_out != NULL the angles are then finalised from the accumulated
+ * moments with `estimator`: centred covariance [[a, c], [c, b]] of the pair,
+ *   phi_k = atan2(a - b, 2c) / 2, wrapped into (-pi/4, pi/4]
+ * (0 for a degenerate pair or no samples), written as float[head_dim/2].
+ *
+ * q may be NULL (Q stream not accumulated); then estimator must be K_ONLY.
+ * n_tokens == 0 only finalises (if angles_out != NULL).
+ * Allocates a scratch buffer of at most 2 * 1024 * head_dim/2 * 5 doubles
+ * stream-ordered (hipMallocAsync / hipFreeAsync) on `stream`. */
+int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
+                         const int32_t* pos, int64_t n_tokens, int32_t estimator,
+                         double* moments, float* angles_out, void* stream);
+
+/* rrp_quant_error_stats -- the diagnostic pass ("contributions" and "results"
+ * sections: K range and relative quantisation error along the block-Hadamard
+ * support interpolation).  Transforms every K row as rrp_rotate_quantize_qk
+ * does (same angles, support_b, group), quantises and dequantises it
+ * (yhat = code * s_h) and writes
+ *   stats_out  double[8] = { E = sum (yhat - y)^2, N = sum y^2,
+ *                            sum of group max|y|, max of group max|y|,
+ *                            sum of group (max y - min y), n_groups, n_rows, 0 }
+ * (overwritten).  Relative error = sqrt(E / N); mean K range = [2] / [5].
+ * Reduced in a fixed order (bit-reproducible).  Allocates a stream-ordered
+ * scratch buffer of at most 1024 * 8 doubles on `stream`. */
+int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
+                          int64_t n_tokens, const float* angles, int32_t support_b, int32_t group,
+                          double* stats_out, void* stream);
+
+/* Host: static description of a status code. */
+const char* rrp_status_string(int status);
+
+/* Host: library version as major * 10000 + minor * 100 + patch. */
+int rrp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RRP_H */

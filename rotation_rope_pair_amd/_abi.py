@@ -1,0 +1,68 @@
+"""ctypes declarations of the C-ABI in include/rrp.h (argument marshalling only).
+
+The HIP library must have been built (``python rotation_rope_pair_amd/build.py``
+or ``__graft_entry__.build()``); loading fails loudly otherwise -- there is no
+fallback implementation.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librrp.so")
+
+RRP_OK, RRP_ERR_INVALID_ARG, RRP_ERR_MISALIGNED, RRP_ERR_UNSUPPORTED, RRP_ERR_HIP = range(5)
+RRP_F32, RRP_BF16 = 0, 1
+RRP_EST_DEFAULT, RRP_EST_K_ONLY, RRP_EST_STREAM_BALANCED = 0, 1, 2
+RRP_ROPE_HALF_SPLIT, RRP_ROPE_INTERLEAVED = 0, 1
+
+# Symbols declared in include/rrp.h.
+EXPORTS = ("rrp_rotate_quantize_qk", "rrp_calibrate_angles", "rrp_quant_error_stats",
+           "rrp_status_string", "rrp_version")
+
+
+class RrpShape(ctypes.Structure):
+    _fields_ = [
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rope_layout", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+    ]
+
+
+class RrpError(RuntimeError):
+    def __init__(self, func, status, msg):
+        super().__init__(f"{func} failed: {msg} (status {status})")
+        self.status = status
+
+
+_LIB = None
+
+
+def load():
+    """Load librrp.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"HIP library not built: {LIB_PATH} is missing; run rotation_rope_pair_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    sp = ctypes.POINTER(RrpShape)
+    L.rrp_rotate_quantize_qk.argtypes = [sp, i32, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, i64,
+                                         vp, vp, vp, vp]
+    L.rrp_calibrate_angles.argtypes = [sp, i32, vp, vp, vp, i64, i32, vp, vp, vp]
+    L.rrp_quant_error_stats.argtypes = [sp, i32, vp, vp, i64, vp, i32, i32, vp, vp]
+    for f in ("rrp_rotate_quantize_qk", "rrp_calibrate_angles", "rrp_quant_error_stats"):
+        getattr(L, f).restype = ctypes.c_int
+    L.rrp_status_string.argtypes = [ctypes.c_int]
+    L.rrp_status_string.restype = ctypes.c_char_p
+    L.rrp_version.argtypes = []
+    L.rrp_version.restype = ctypes.c_int
+    _LIB = L
+    return L
+
+
+def check(func, status):
+    if status != RRP_OK:
+        raise RrpError(func, status, load().rrp_status_string(status).decode())

@@ -1,0 +1,141 @@
+"""Torch-facing binding of the C-ABI: passes device pointers, sizes and the
+current HIP stream.  Every step of the path runs in the HIP kernels; this
+module only checks that each tensor is a contiguous device tensor of the size
+the kernels will touch, so no launch can read or write outside a buffer.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _abi
+from ._abi import (RRP_BF16, RRP_EST_DEFAULT, RRP_EST_K_ONLY, RRP_EST_STREAM_BALANCED, RRP_F32,
+                   RRP_ROPE_HALF_SPLIT, RRP_ROPE_INTERLEAVED, RrpError, RrpShape)
+
+ESTIMATORS = {"default": RRP_EST_DEFAULT, "k_only": RRP_EST_K_ONLY, "stream_balanced": RRP_EST_STREAM_BALANCED}
+
+
+def layer_shape(n_q_heads: int, n_kv_heads: int, head_dim: int, rope_theta: float,
+                rope_layout: int = RRP_ROPE_HALF_SPLIT) -> RrpShape:
+    return RrpShape(int(n_q_heads), int(n_kv_heads), int(head_dim), int(rope_layout), float(rope_theta))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RRP_F32
+    if t.dtype == torch.bfloat16:
+        return RRP_BF16
+    raise TypeError(f"Q/K tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, numel: Optional[int] = None, dtype=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def new_kv4_cache(n_slots: int, n_kv_heads: int, head_dim: int, group: int, device="cuda"):
+    """Allocate an empty KV4 K cache: packed codes uint8 [n_slots][Hkv][d/2] and
+    fp16 scales [n_slots][Hkv][d/group]."""
+    codes = torch.zeros((n_slots, n_kv_heads, head_dim // 2), dtype=torch.uint8, device=device)
+    scales = torch.zeros((n_slots, n_kv_heads, head_dim // group), dtype=torch.float16, device=device)
+    return codes, scales
+
+
+def new_moments(head_dim: int, device="cuda") -> torch.Tensor:
+    """Zeroed calibration state double[head_dim/2][2][6]."""
+    return torch.zeros((head_dim // 2, 2, 6), dtype=torch.float64, device=device)
+
+
+def rotate_quantize_qk(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor, pos: torch.Tensor, *,
+                       support_b: int, group: int, k_codes: torch.Tensor, k_scales: torch.Tensor,
+                       angles: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None,
+                       slot_mapping: Optional[torch.Tensor] = None, n_slots: Optional[int] = None,
+                       q_rot_f32: Optional[torch.Tensor] = None, k_rot_f32: Optional[torch.Tensor] = None,
+                       k_scale_f32: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue rrp_rotate_quantize_qk (see include/rrp.h)."""
+    L = _abi.load()
+    d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    T = int(pos.numel())
+    dt = k.dtype
+    dev = k.device
+    if n_slots is None:
+        n_slots = int(k_codes.shape[0])
+    if n_slots * hk * (d // 2) > k_codes.numel():
+        raise ValueError("k_codes is smaller than n_slots * n_kv_heads * head_dim / 2")
+    args = [
+        ctypes.byref(shape), _dtype_code(k),
+        _dev(q, "q", T * hq * d, dt, dev), _dev(k, "k", T * hk * d, dt, dev),
+        _dev(pos, "pos", T, torch.int32, dev), T,
+        _dev(angles, "angles", d // 2, torch.float32, dev), int(support_b), int(group),
+        _dev(q_out, "q_out", T * hq * d, dt, dev),
+        _dev(k_codes, "k_codes", n_slots * hk * (d // 2), torch.uint8, dev),
+        _dev(k_scales, "k_scales", n_slots * hk * max(1, d // max(1, int(group))),
+             (torch.float16, torch.int16), dev),
+        _dev(slot_mapping, "slot_mapping", T, torch.int64, dev), int(n_slots),
+        _dev(q_rot_f32, "q_rot_f32", T * hq * d, torch.float32, dev),
+        _dev(k_rot_f32, "k_rot_f32", T * hk * d, torch.float32, dev),
+        _dev(k_scale_f32, "k_scale_f32", T * hk * max(1, d // max(1, int(group))), torch.float32, dev),
+        _stream_ptr(stream, dev),
+    ]
+    _abi.check("rrp_rotate_quantize_qk", L.rrp_rotate_quantize_qk(*args))
+
+
+def calibrate_angles(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor, pos: torch.Tensor, *,
+                     moments: torch.Tensor, estimator="default", angles_out: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """Enqueue rrp_calibrate_angles: accumulate pair moments into `moments` and,
+    if angles_out is given, finalise the shared angles (see include/rrp.h)."""
+    L = _abi.load()
+    est = ESTIMATORS[estimator] if isinstance(estimator, str) else int(estimator)
+    d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    T = int(pos.numel())
+    dt, dev = k.dtype, k.device
+    args = [
+        ctypes.byref(shape), _dtype_code(k),
+        _dev(q, "q", T * hq * d, dt, dev), _dev(k, "k", T * hk * d, dt, dev),
+        _dev(pos, "pos", T, torch.int32, dev), T, est,
+        _dev(moments, "moments", (d // 2) * 12, torch.float64, dev),
+        _dev(angles_out, "angles_out", d // 2, torch.float32, dev),
+        _stream_ptr(stream, dev),
+    ]
+    _abi.check("rrp_calibrate_angles", L.rrp_calibrate_angles(*args))
+
+
+def quant_error_stats(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, support_b: int, group: int,
+                      stats_out: torch.Tensor, angles: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue rrp_quant_error_stats into stats_out (double[8], see include/rrp.h)."""
+    L = _abi.load()
+    d, hk = shape.head_dim, shape.n_kv_heads
+    T = int(pos.numel())
+    dt, dev = k.dtype, k.device
+    args = [
+        ctypes.byref(shape), _dtype_code(k), _dev(k, "k", T * hk * d, dt, dev),
+        _dev(pos, "pos", T, torch.int32, dev), T,
+        _dev(angles, "angles", d // 2, torch.float32, dev), int(support_b), int(group),
+        _dev(stats_out, "stats_out", 8, torch.float64, dev), _stream_ptr(stream, dev),
+    ]
+    _abi.check("rrp_quant_error_stats", L.rrp_quant_error_stats(*args))
+
+
+__all__ = ["layer_shape", "rotate_quantize_qk", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
+           "new_moments", "RrpError", "RrpShape", "ESTIMATORS", "RRP_F32", "RRP_BF16",
+           "RRP_ROPE_HALF_SPLIT", "RRP_ROPE_INTERLEAVED"]

@@ -1,0 +1,201 @@
+// rrp_abi.hip -- the C-ABI entry points (include/rrp.h): host-side validation,
+// RoPE frequency table, stream-ordered scratch and kernel dispatch.
+//
+// Every check runs before anything is enqueued, so an error return leaves the
+// stream untouched.  The RoPE frequencies are evaluated here on the host in
+// fp64 (libm pow) and rounded once to fp32; they travel to the kernels inside
+// the kernel argument block.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "rrp.h"
+#include "rrp_kernels.hpp"
+
+#define RRP_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int check_shape(const rrp_shape* s, int32_t dtype) {
+    if (s == nullptr) return RRP_ERR_INVALID_ARG;
+    if (dtype != RRP_F32 && dtype != RRP_BF16) return RRP_ERR_INVALID_ARG;
+    if (s->n_q_heads < 0 || s->n_kv_heads < 1) return RRP_ERR_INVALID_ARG;
+    if (s->rope_layout != RRP_ROPE_HALF_SPLIT && s->rope_layout != RRP_ROPE_INTERLEAVED) return RRP_ERR_INVALID_ARG;
+    if (!(s->rope_theta > 0.0) || !isfinite(s->rope_theta)) return RRP_ERR_INVALID_ARG;
+    if (s->head_dim < 2 || (s->head_dim & 1)) return RRP_ERR_INVALID_ARG;
+    if (s->head_dim != 64 && s->head_dim != 128) return RRP_ERR_UNSUPPORTED;
+    return RRP_OK;
+}
+
+int check_b_g(const rrp_shape* s, int32_t support_b, int32_t group) {
+    if (!is_pow2(support_b) || support_b > s->head_dim) return RRP_ERR_INVALID_ARG;
+    if (!is_pow2(group) || group < 2 || group > s->head_dim) return RRP_ERR_INVALID_ARG;
+    return RRP_OK;
+}
+
+void fill_inv_freq(const rrp_shape* s, float* out) {
+    for (int k = 0; k < rrp::kMaxPairs; ++k)
+        out[k] = k < s->head_dim / 2 ? (float)pow(s->rope_theta, -2.0 * (double)k / (double)s->head_dim) : 0.0f;
+}
+
+// Stream-ordered scratch that is released on the same stream after use.
+struct Scratch {
+    void* p = nullptr;
+    hipStream_t st = nullptr;
+    hipError_t alloc(size_t bytes, hipStream_t stream) {
+        st = stream;
+        return hipMallocAsync(&p, bytes, stream);
+    }
+    ~Scratch() {
+        if (p) (void)hipFreeAsync(p, st);
+    }
+};
+
+}  // namespace
+
+RRP_EXPORT int rrp_version(void) { return kVersion; }
+
+RRP_EXPORT const char* rrp_status_string(int status) {
+    switch (status) {
+        case RRP_OK: return "ok";
+        case RRP_ERR_INVALID_ARG: return "invalid argument";
+        case RRP_ERR_MISALIGNED: return "misaligned pointer";
+        case RRP_ERR_UNSUPPORTED: return "unsupported configuration";
+        case RRP_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+RRP_EXPORT int rrp_rotate_quantize_qk(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
+                                      const int32_t* pos, int64_t n_tokens, const float* angles,
+                                      int32_t support_b, int32_t group, void* q_out, uint8_t* k_codes,
+                                      uint16_t* k_scales, const int64_t* slot_mapping, int64_t n_slots,
+                                      float* q_rot_f32, float* k_rot_f32, float* k_scale_f32, void* stream) {
+    int st = check_shape(shape, dtype);
+    if (st != RRP_OK) return st;
+    if ((st = check_b_g(shape, support_b, group)) != RRP_OK) return st;
+    if (n_tokens < 0 || n_slots < 0) return RRP_ERR_INVALID_ARG;
+    if (k == nullptr || pos == nullptr || k_codes == nullptr || k_scales == nullptr) return RRP_ERR_INVALID_ARG;
+    if ((q_out != nullptr || q_rot_f32 != nullptr) && q == nullptr) return RRP_ERR_INVALID_ARG;
+    if (slot_mapping == nullptr && n_slots < n_tokens) return RRP_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 16) || !aligned(q_rot_f32, 16) ||
+        !aligned(k_rot_f32, 16) || !aligned(k_scale_f32, 4) || !aligned(pos, 4) || !aligned(angles, 4) ||
+        !aligned(k_codes, dtype == RRP_F32 ? 2 : 4) || !aligned(k_scales, 2) || !aligned(slot_mapping, 8))
+        return RRP_ERR_MISALIGNED;
+    if (n_tokens == 0) return RRP_OK;
+
+    rrp::RotateArgs a{};
+    a.q = q;
+    a.k = k;
+    a.pos = pos;
+    a.angles = angles;
+    a.q_out = q_out;
+    a.k_codes = k_codes;
+    a.k_scales = k_scales;
+    a.slot_mapping = slot_mapping;
+    a.q_dbg = q_rot_f32;
+    a.k_dbg = k_rot_f32;
+    a.s_dbg = k_scale_f32;
+    a.n_tokens = n_tokens;
+    a.n_slots = n_slots;
+    a.hq = shape->n_q_heads;
+    a.hq_rows = (q != nullptr && (q_out != nullptr || q_rot_f32 != nullptr)) ? shape->n_q_heads : 0;
+    a.hk = shape->n_kv_heads;
+    a.support_b = support_b;
+    a.group = group;
+    a.rsqrt_b = 1.0 / sqrt((double)support_b);
+    fill_inv_freq(shape, a.inv_freq);
+    hipError_t e = rrp::launch_rotate_quantize(a, dtype, shape->head_dim, shape->rope_layout, (hipStream_t)stream);
+    return e == hipSuccess ? RRP_OK : RRP_ERR_HIP;
+}
+
+RRP_EXPORT int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
+                                    const int32_t* pos, int64_t n_tokens, int32_t estimator,
+                                    double* moments, float* angles_out, void* stream) {
+    int st = check_shape(shape, dtype);
+    if (st != RRP_OK) return st;
+    if (estimator < RRP_EST_DEFAULT || estimator > RRP_EST_STREAM_BALANCED) return RRP_ERR_INVALID_ARG;
+    if (n_tokens < 0 || moments == nullptr) return RRP_ERR_INVALID_ARG;
+    if (n_tokens > 0 && (k == nullptr || pos == nullptr)) return RRP_ERR_INVALID_ARG;
+    if (q == nullptr && estimator != RRP_EST_K_ONLY && n_tokens > 0) return RRP_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(pos, 4) || !aligned(moments, 8) || !aligned(angles_out, 4))
+        return RRP_ERR_MISALIGNED;
+    const hipStream_t s = (hipStream_t)stream;
+    const int P = shape->head_dim / 2;
+
+    rrp::CalibFinalArgs f{};
+    f.moments = moments;
+    f.angles_out = angles_out;
+    f.n_pairs = P;
+    f.estimator = estimator;
+    Scratch scratch;
+    if (n_tokens > 0) {
+        int nbq = 0, nbk = 0;
+        const bool with_q = q != nullptr && shape->n_q_heads > 0;
+        const int nb = rrp::calib_blocks(n_tokens, with_q, shape->n_q_heads, shape->n_kv_heads, &nbq, &nbk);
+        if (scratch.alloc((size_t)nb * P * 5 * sizeof(double), s) != hipSuccess) return RRP_ERR_HIP;
+        rrp::CalibArgs a{};
+        a.q = q;
+        a.k = k;
+        a.pos = pos;
+        a.partials = static_cast<double*>(scratch.p);
+        a.n_tokens = n_tokens;
+        a.hq = shape->n_q_heads;
+        a.hk = shape->n_kv_heads;
+        a.nbq = nbq;
+        a.nbk = nbk;
+        fill_inv_freq(shape, a.inv_freq);
+        if (rrp::launch_calibrate(a, dtype, shape->head_dim, shape->rope_layout, s) != hipSuccess) return RRP_ERR_HIP;
+        f.partials = a.partials;
+        f.nbq = nbq;
+        f.nbk = nbk;
+        f.n_rows_q = (double)n_tokens * shape->n_q_heads;
+        f.n_rows_k = (double)n_tokens * shape->n_kv_heads;
+    } else if (angles_out == nullptr) {
+        return RRP_OK;
+    }
+    return rrp::launch_calibrate_final(f, s) == hipSuccess ? RRP_OK : RRP_ERR_HIP;
+}
+
+RRP_EXPORT int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
+                                     int64_t n_tokens, const float* angles, int32_t support_b, int32_t group,
+                                     double* stats_out, void* stream) {
+    int st = check_shape(shape, dtype);
+    if (st != RRP_OK) return st;
+    if ((st = check_b_g(shape, support_b, group)) != RRP_OK) return st;
+    if (n_tokens < 0 || stats_out == nullptr) return RRP_ERR_INVALID_ARG;
+    if (n_tokens > 0 && (k == nullptr || pos == nullptr)) return RRP_ERR_INVALID_ARG;
+    if (!aligned(k, 16) || !aligned(pos, 4) || !aligned(angles, 4) || !aligned(stats_out, 8))
+        return RRP_ERR_MISALIGNED;
+    const hipStream_t s = (hipStream_t)stream;
+    rrp::StatsFinalArgs f{};
+    f.stats_out = stats_out;
+    f.n_rows = (double)n_tokens * shape->n_kv_heads;
+    f.n_groups = f.n_rows * (shape->head_dim / group);
+    Scratch scratch;
+    if (n_tokens > 0) {
+        const int nb = rrp::stats_blocks(n_tokens);
+        if (scratch.alloc((size_t)nb * 5 * sizeof(double), s) != hipSuccess) return RRP_ERR_HIP;
+        rrp::StatsArgs a{};
+        a.k = k;
+        a.pos = pos;
+        a.angles = angles;
+        a.partials = static_cast<double*>(scratch.p);
+        a.n_tokens = n_tokens;
+        a.hk = shape->n_kv_heads;
+        a.support_b = support_b;
+        a.group = group;
+        a.rsqrt_b = 1.0 / sqrt((double)support_b);
+        fill_inv_freq(shape, a.inv_freq);
+        if (rrp::launch_stats(a, nb, dtype, shape->head_dim, shape->rope_layout, s) != hipSuccess) return RRP_ERR_HIP;
+        f.partials = a.partials;
+        f.n_blocks = nb;
+    }
+    return rrp::launch_stats_final(f, s) == hipSuccess ? RRP_OK : RRP_ERR_HIP;
+}

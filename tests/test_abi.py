@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every entry point include/rrp.h declares, and
+rejects bad arguments on the host before touching the GPU (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rrp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from rotation_rope_pair_amd import _abi
+    if not os.path.exists(_abi.LIB_PATH):
+        from rotation_rope_pair_amd import build
+        build.build()
+    return _abi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rrp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["rrp_calibrate_angles", "rrp_quant_error_stats", "rrp_rotate_quantize_qk",
+                                           "rrp_status_string", "rrp_version"])
+
+
+def test_library_exports_exactly_the_declared_symbols(lib):
+    from rotation_rope_pair_amd import _abi
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if " T " in l and l.split()[-1].startswith("rrp_")})
+    assert exported == declared_functions()
+    for name in declared_functions():
+        assert hasattr(lib, name)
+    assert sorted(_abi.EXPORTS) == declared_functions()
+
+
+def test_version_and_status_strings(lib):
+    assert lib.rrp_version() == 10000
+    assert lib.rrp_status_string(0) == b"ok"
+    assert lib.rrp_status_string(2) == b"misaligned pointer"
+    assert lib.rrp_status_string(99) == b"unknown status"
+
+
+def _shape(hq=32, hk=8, d=128, layout=0, theta=5e5):
+    from rotation_rope_pair_amd._abi import RrpShape
+    return RrpShape(hq, hk, d, layout, theta)
+
+
+P16 = ctypes.c_void_p(1 << 20)       # a 16-byte aligned, never dereferenced address
+P2 = ctypes.c_void_p((1 << 20) + 2)   # 2-byte aligned only
+
+
+def rot(lib, shape=None, dtype=1, q=None, k=P16, pos=P16, T=4, angles=None, b=128, g=128, q_out=None,
+        codes=P16, scales=P16, slots=None, n_slots=4, qd=None, kd=None, sd=None):
+    return lib.rrp_rotate_quantize_qk(ctypes.byref(shape or _shape()), dtype, q, k, pos, T, angles, b, g, q_out,
+                                      codes, scales, slots, n_slots, qd, kd, sd, None)
+
+
+def test_rotate_validation(lib):
+    assert rot(lib, T=0, n_slots=0) == 0                          # empty batch: no-op
+    assert lib.rrp_rotate_quantize_qk(None, 1, None, P16, P16, 4, None, 128, 128, None, P16, P16, None, 4,
+                                      None, None, None, None) == 1
+    assert rot(lib, dtype=7) == 1
+    assert rot(lib, shape=_shape(d=96)) == 3
+    assert rot(lib, shape=_shape(d=65)) == 1
+    assert rot(lib, shape=_shape(hk=0)) == 1
+    assert rot(lib, shape=_shape(layout=5)) == 1
+    assert rot(lib, shape=_shape(theta=-1.0)) == 1
+    assert rot(lib, shape=_shape(theta=float("inf"))) == 1
+    assert rot(lib, b=3) == 1 and rot(lib, b=256) == 1 and rot(lib, b=0) == 1
+    assert rot(lib, g=1) == 1 and rot(lib, g=96) == 1 and rot(lib, g=256) == 1
+    assert rot(lib, T=-1) == 1
+    assert rot(lib, k=None) == 1 and rot(lib, pos=None) == 1
+    assert rot(lib, codes=None) == 1 and rot(lib, scales=None) == 1
+    assert rot(lib, q_out=P16) == 1                               # q_out needs q
+    assert rot(lib, n_slots=3) == 1                               # identity slots need n_slots >= T
+    assert rot(lib, k=P2) == 2 and rot(lib, q=P2, q_out=P16) == 2
+    assert rot(lib, codes=P2) == 2 and rot(lib, kd=P2) == 2
+    assert rot(lib, slots=ctypes.c_void_p((1 << 20) + 4)) == 2
+
+
+def test_calibrate_validation(lib):
+    def cal(shape=None, dtype=1, q=P16, k=P16, pos=P16, T=4, est=0, mom=P16, ang=None):
+        return lib.rrp_calibrate_angles(ctypes.byref(shape or _shape()), dtype, q, k, pos, T, est, mom, ang, None)
+    assert cal(est=3) == 1 and cal(est=-1) == 1
+    assert cal(mom=None) == 1
+    assert cal(q=None, est=0) == 1 and cal(q=None, est=2) == 1    # Q needed by these estimators
+    assert cal(k=None) == 1 and cal(pos=None) == 1 and cal(T=-2) == 1
+    assert cal(shape=_shape(d=256)) == 3
+    assert cal(k=P2) == 2 and cal(mom=ctypes.c_void_p((1 << 20) + 4)) == 2
+    assert cal(T=0, q=None, k=None, pos=None, ang=None) == 0      # nothing to do
+
+
+def test_stats_validation(lib):
+    def stt(T=4, k=P16, pos=P16, b=128, g=128, out=P16):
+        return lib.rrp_quant_error_stats(ctypes.byref(_shape()), 1, k, pos, T, None, b, g, out, None)
+    assert stt(out=None) == 1 and stt(k=None) == 1 and stt(b=5) == 1 and stt(g=3) == 1
+    assert stt(out=ctypes.c_void_p((1 << 20) + 4)) == 2
+
+
+def test_binding_rejects_host_tensors_before_any_launch():
+    torch = pytest.importorskip("torch")
+    import rotation_rope_pair_amd as rrp
+    shape = rrp.layer_shape(2, 1, 64, 5e5)
+    k = torch.zeros((4, 1, 64), dtype=torch.float32)
+    pos = torch.zeros(4, dtype=torch.int32)
+    codes = torch.zeros((4, 1, 32), dtype=torch.uint8)
+    scales = torch.zeros((4, 1, 1), dtype=torch.float16)
+    with pytest.raises(ValueError, match="device"):
+        rrp.rotate_quantize_qk(shape, None, k, pos, support_b=64, group=64, k_codes=codes, k_scales=scales)

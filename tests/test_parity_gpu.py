@@ -1,0 +1,368 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C-ABI.
+
+Inputs are the seeded synthetic workloads (rotation_rope_pair_amd/workloads.py);
+the same bytes go to the GPU and to the oracle.  Small workloads are compared
+element by element in full; the large ones run at their full size on the GPU
+(in the launch configuration the benchmark times) and are compared on a
+sample of tokens that the oracle evaluates one by one.  Tolerances: see
+oracle/compare.py.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+from oracle import compare as C  # noqa: E402
+import rotation_rope_pair_amd as rrp  # noqa: E402
+from rotation_rope_pair_amd import workloads as W  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU-only container
+    pytest.skip("no GPU", allow_module_level=True)
+
+DEV = torch.device("cuda:0")
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def to_dev(a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bits(t):
+    """bf16 / fp16 device tensor -> uint16 numpy bit patterns."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def shape_of(w, layout=0):
+    return rrp.layer_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.rope_theta, layout)
+
+
+def oshape_of(w, layout=0, hq=None):
+    return O.shape(w.n_q_heads if hq is None else hq, w.n_kv_heads, w.head_dim, w.rope_theta, layout)
+
+
+def random_angles(P, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.uniform(-math.pi / 4, math.pi / 4, P).astype(np.float32)
+
+
+def sample_tokens(T, n, seed=0):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    head = np.arange(min(64, n // 4))
+    tail = np.arange(T - min(64, n // 4), T)
+    mid = rng.choice(np.arange(head.size, T - tail.size), n - head.size - tail.size, replace=False)
+    return np.unique(np.concatenate([head, mid, tail]))
+
+
+def run_rotate(w, inp, angles, b, g, *, debug=True, in_place=False, with_q=True, layout=0,
+               q_dev=None, k_dev=None, pos_dev=None):
+    d, hq, hk = w.head_dim, w.n_q_heads, w.n_kv_heads
+    q = q_dev if q_dev is not None else (to_dev(inp["q"]) if with_q else None)
+    k = k_dev if k_dev is not None else to_dev(inp["k"])
+    pos = pos_dev if pos_dev is not None else to_dev(inp["pos"])
+    T = int(pos.numel())
+    n_slots = inp.get("n_slots", T)
+    codes, scales = rrp.new_kv4_cache(n_slots, hk, d, g, DEV)
+    q_out = (q if in_place else torch.empty_like(q)) if with_q else None
+    dbg = {}
+    if debug:
+        if with_q:
+            dbg["q_rot_f32"] = torch.empty((T, hq, d), dtype=torch.float32, device=DEV)
+        dbg["k_rot_f32"] = torch.empty((T, hk, d), dtype=torch.float32, device=DEV)
+        dbg["k_scale_f32"] = torch.empty((T, hk, d // g), dtype=torch.float32, device=DEV)
+    sm = to_dev(inp.get("slot_mapping"))
+    rrp.rotate_quantize_qk(shape_of(w, layout), q, k, pos, support_b=b, group=g, k_codes=codes, k_scales=scales,
+                           angles=None if angles is None else to_dev(angles), q_out=q_out, slot_mapping=sm,
+                           n_slots=n_slots, **dbg)
+    torch.cuda.synchronize()
+    return {"q_out": q_out, "codes": codes, "scales": scales, **dbg}
+
+
+def check_rotate(w, inp, out, angles, b, g, idx, *, layout=0, with_q=True):
+    """Compare GPU outputs of the tokens `idx` with the oracle run on just those tokens."""
+    d, hq, hk = w.head_dim, w.n_q_heads, w.n_kv_heads
+    idx = np.asarray(idx)
+    q = inp["q"][idx] if with_q else None
+    ref = O.rotate_quantize_qk(oshape_of(w, layout, hq if with_q else 0), q, inp["k"][idx], inp["pos"][idx],
+                               angles, b, g)
+    sm = inp.get("slot_mapping")
+    slots = idx if sm is None else sm[idx]
+    sl = torch.from_numpy(slots.astype(np.int64)).to(DEV)
+    it = torch.from_numpy(idx.astype(np.int64)).to(DEV)
+    fmt = "f32" if w.dtype == "f32" else "bf16"
+    rep = {}
+    if with_q and out["q_out"] is not None:
+        qo = out["q_out"].index_select(0, it)
+        qo = bits(qo) if fmt == "bf16" else qo.cpu().numpy()
+        C.check_q_out(qo, ref["q_rot"], fmt)
+        if "q_rot_f32" in out:
+            rep["q_row_rel_err"] = C.row_rel_err(out["q_rot_f32"].index_select(0, it).cpu().numpy(), ref["q_rot"])
+            assert rep["q_row_rel_err"] <= C.ROW_REL_TOL, rep
+    codes = out["codes"].index_select(0, sl).cpu().numpy().reshape(-1, d // 2)
+    scales = bits(out["scales"].index_select(0, sl)).reshape(-1, d // g)
+    kw = {}
+    if "k_rot_f32" in out:
+        kw = dict(k_rot_gpu=out["k_rot_f32"].index_select(0, it).cpu().numpy().reshape(-1, d),
+                  s32_gpu=out["k_scale_f32"].index_select(0, it).cpu().numpy().reshape(-1, d // g),
+                  s32_ref=ref["k_scale32"].reshape(-1, d // g))
+    rep.update(C.compare_k(codes, scales, ref["k_rot"].reshape(-1, d), ref["k_scales"].reshape(-1, d // g),
+                           ref["k_codes"].reshape(-1, d // 2), g, **kw))
+    return rep
+
+
+_INPUTS = {}
+
+
+def inputs(n):
+    if n not in _INPUTS:
+        _INPUTS[n] = W.make_inputs(n)
+    return _INPUTS[n]
+
+
+# ---------------------------------------------------------------------------
+# rotate + quantise
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,b", [(1, 1), (1, 2), (1, 64), (2, 1), (2, 2), (2, 4), (2, 8), (2, 16), (2, 32), (2, 64)])
+def test_rotate_parity_small_workloads_in_full(n, b):
+    w, inp = W.WORKLOADS[n], inputs(n)
+    ang = random_angles(w.n_pairs, 100 + n)
+    out = run_rotate(w, inp, ang, b, w.group)
+    rep = check_rotate(w, inp, out, ang, b, w.group, np.arange(w.n_tokens))
+    print(f"workload {n} b={b}: {rep}")
+
+
+def test_rotate_parity_without_pair_angles():
+    w, inp = W.WORKLOADS[2], inputs(2)
+    out = run_rotate(w, inp, None, 64, 64)
+    print(check_rotate(w, inp, out, None, 64, 64, np.arange(w.n_tokens)))
+
+
+def test_rotate_parity_llama3b_layer_sampled():
+    w, inp = W.WORKLOADS[3], inputs(3)
+    ang = random_angles(w.n_pairs, 103)
+    out = run_rotate(w, inp, ang, 128, 128)
+    print(check_rotate(w, inp, out, ang, 128, 128, sample_tokens(w.n_tokens, 1024, 3)))
+
+
+@pytest.mark.parametrize("b", [2, 128])
+def test_rotate_parity_decode_slot_scatter(b):
+    """Decode batch: 256 tokens at random positions scattered into a 256 x 32768-slot
+    cache; only the mapped slots are written."""
+    w, inp = W.WORKLOADS[5], inputs(5)
+    ang = random_angles(w.n_pairs, 105)
+    out = run_rotate(w, inp, ang, b, w.group)
+    print(check_rotate(w, inp, out, ang, b, w.group, np.arange(w.n_tokens)))
+    written = int(torch.count_nonzero(out["scales"]).item())
+    sl = torch.from_numpy(inp["slot_mapping"]).to(DEV)
+    assert written == int(torch.count_nonzero(out["scales"].index_select(0, sl)).item())
+    nz_codes = int(torch.count_nonzero(out["codes"]).item())
+    assert nz_codes == int(torch.count_nonzero(out["codes"].index_select(0, sl)).item())
+
+
+def test_rotate_parity_prefill_128k_bench_launch():
+    """Full 131072-token prefill in exactly the call the benchmark times (no debug
+    outputs), checked on 2048 sampled tokens."""
+    w, inp = W.WORKLOADS[4], inputs(4)
+    ang = random_angles(w.n_pairs, 104)
+    out = run_rotate(w, inp, ang, 128, 128, debug=False)
+    rep = check_rotate(w, inp, out, ang, 128, 128, sample_tokens(w.n_tokens, 2048, 4))
+    print(rep)
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("n", [1, 2, 3])
+def test_rotate_parity_rope_layouts(n, layout):
+    w, inp = W.WORKLOADS[n], inputs(n)
+    T = min(w.n_tokens, 512)
+    sub = {k: (v[:T] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    sub["n_slots"] = T
+    ang = random_angles(w.n_pairs, 200 + n)
+    b = w.head_dim
+    out = run_rotate(w, sub, ang, b, w.group, layout=layout)
+    print(check_rotate(w, sub, out, ang, b, w.group, np.arange(T), layout=layout))
+
+
+@pytest.mark.parametrize("n,g", [(1, 2), (1, 4), (1, 8), (1, 32), (3, 2), (3, 4), (3, 8), (3, 16), (3, 32), (3, 64)])
+def test_rotate_parity_group_sizes(n, g):
+    w, inp = W.WORKLOADS[n], inputs(n)
+    T = min(w.n_tokens, 256)
+    sub = {k: (v[:T] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    sub["n_slots"] = T
+    ang = random_angles(w.n_pairs, 300 + g)
+    for b in (2, w.head_dim):
+        out = run_rotate(w, sub, ang, b, g)
+        print(n, g, b, check_rotate(w, sub, out, ang, b, g, np.arange(T)))
+
+
+@pytest.mark.parametrize("T", [1, 3, 5, 4097])
+def test_rotate_ragged_token_counts(T):
+    w = W.WORKLOADS[3]
+    inp = W.make_inputs(3, n_tokens=T)
+    ang = random_angles(w.n_pairs, 400)
+    out = run_rotate(w, inp, ang, 128, 128)
+    print(T, check_rotate(w, inp, out, ang, 128, 128, np.arange(T)))
+
+
+def test_rotate_in_place_and_k_only():
+    w, inp = W.WORKLOADS[2], inputs(2)
+    ang = random_angles(w.n_pairs, 500)
+    out = run_rotate(w, inp, ang, 16, 64, in_place=True)
+    check_rotate(w, inp, out, ang, 16, 64, np.arange(w.n_tokens))
+    out2 = run_rotate(w, inp, ang, 16, 64, with_q=False)
+    check_rotate(w, inp, out2, ang, 16, 64, np.arange(w.n_tokens), with_q=False)
+    assert torch.equal(out["codes"], out2["codes"]) and torch.equal(out["scales"], out2["scales"])
+
+
+def test_rotate_degenerate_rows():
+    """All-zero rows (scale 0, codes 0), rows so small the fp16 scale underflows,
+    rows so large it saturates, and padding slots (-1, out of range)."""
+    w = W.WORKLOADS[3]
+    T = 16
+    inp = W.make_inputs(3, n_tokens=T)
+    k = inp["k"].copy()
+    import torch as _t
+    def bf(x):
+        return _t.from_numpy(np.asarray(x, np.float32)).to(_t.bfloat16).view(_t.int16).numpy().view(np.uint16)
+    k[0] = 0
+    k[1] = bf(np.full((w.n_kv_heads, w.head_dim), 1e-9))
+    k[2] = bf(np.full((w.n_kv_heads, w.head_dim), 3e5) * np.sign(np.arange(w.head_dim) - 63.5))
+    k[3, 0] = bf(np.eye(w.head_dim)[5] * 100.0)
+    inp["k"] = k
+    slots = np.arange(T, dtype=np.int64)
+    slots[4] = -1
+    slots[5] = 10 ** 9
+    inp["slot_mapping"] = slots
+    inp["n_slots"] = T
+    ang = random_angles(w.n_pairs, 600)
+    for b in (1, 2, 128):
+        out = run_rotate(w, inp, ang, b, 64)
+        keep = np.array([t for t in range(T) if 0 <= slots[t] < T])
+        print(b, check_rotate(w, inp, out, ang, b, 64, keep))
+        assert not out["codes"][4].any() and not out["scales"][4].any()
+        assert not out["codes"][0].any() and not out["scales"][0].any()
+
+
+def test_rotate_is_deterministic():
+    w, inp = W.WORKLOADS[3], inputs(3)
+    ang = random_angles(w.n_pairs, 700)
+    a = run_rotate(w, inp, ang, 128, 128)
+    b = run_rotate(w, inp, ang, 128, 128)
+    for key in ("q_out", "codes", "scales", "q_rot_f32", "k_rot_f32", "k_scale_f32"):
+        assert torch.equal(a[key].view(torch.uint8) if a[key].dtype == torch.bfloat16 else a[key],
+                           b[key].view(torch.uint8) if b[key].dtype == torch.bfloat16 else b[key]), key
+
+
+# ---------------------------------------------------------------------------
+# calibration
+# ---------------------------------------------------------------------------
+
+def run_calib(w, q, k, pos, estimator, layout=0, moments=None):
+    d = w.head_dim
+    mom = moments if moments is not None else rrp.new_moments(d, DEV)
+    ang = torch.empty(d // 2, dtype=torch.float32, device=DEV)
+    rrp.calibrate_angles(shape_of(w, layout), None if q is None else to_dev(q), to_dev(k), to_dev(pos),
+                         moments=mom, estimator=estimator, angles_out=ang)
+    torch.cuda.synchronize()
+    return mom.cpu().numpy(), ang.cpu().numpy()
+
+
+EST = {"default": O.EST_DEFAULT, "k_only": O.EST_K_ONLY, "stream_balanced": O.EST_STREAM_BALANCED}
+
+
+@pytest.mark.parametrize("n,est", [(1, "default"), (2, "default"), (2, "k_only"), (2, "stream_balanced"),
+                                   (3, "default"), (4, "default"), (5, "k_only")])
+def test_calibration_parity(n, est):
+    w = W.WORKLOADS[n]
+    inp = inputs(n)
+    src = inp["calib"] if inp["calib"] is not None else inp
+    q = src["q"] if est != "k_only" else None
+    mom_g, ang_g = run_calib(w, q, src["k"], src["pos"], est)
+    shp = oshape_of(w)
+    mom_r = O.calibrate_moments(shp, q, src["k"], src["pos"])
+    phi64, phi32, abc = O.angles_from_moments(mom_r, EST[est])
+    worst = C.compare_moments(mom_g, mom_r)
+    rep = C.compare_angles(ang_g, phi64, abc)
+    print(f"workload {n} {est}: moments {worst:.2e} {rep}")
+
+
+def test_calibration_accumulates_and_finalises_separately():
+    w, inp = W.WORKLOADS[2], inputs(2)
+    q, k, pos = inp["q"], inp["k"], inp["pos"]
+    mom_all, ang_all = run_calib(w, q, k, pos, "default")
+    mom = rrp.new_moments(w.head_dim, DEV)
+    run_calib(w, q[:700], k[:700], pos[:700], "default", moments=mom)
+    mom2, ang2 = run_calib(w, q[700:], k[700:], pos[700:], "default", moments=mom)
+    C.compare_moments(mom2, mom_all, rel=1e-13)
+    assert np.max(C.angle_diff(ang2, ang_all)) < 1e-6
+    # finalise only (no tokens) with another estimator
+    ang3 = torch.empty(w.n_pairs, dtype=torch.float32, device=DEV)
+    e = torch.empty((0,), dtype=torch.bfloat16, device=DEV)
+    rrp.calibrate_angles(shape_of(w), e, e, torch.empty((0,), dtype=torch.int32, device=DEV), moments=mom,
+                         estimator="stream_balanced", angles_out=ang3)
+    torch.cuda.synchronize()
+    phi64, _, abc = O.angles_from_moments(mom2, O.EST_STREAM_BALANCED)
+    C.compare_angles(ang3.cpu().numpy(), phi64, abc)
+    assert np.array_equal(mom.cpu().numpy(), mom2)
+
+
+def test_calibration_is_deterministic():
+    w, inp = W.WORKLOADS[3], inputs(3)
+    m1, a1 = run_calib(w, inp["q"], inp["k"], inp["pos"], "default")
+    m2, a2 = run_calib(w, inp["q"], inp["k"], inp["pos"], "default")
+    assert np.array_equal(m1, m2) and np.array_equal(a1, a2)
+
+
+# ---------------------------------------------------------------------------
+# diagnostics
+# ---------------------------------------------------------------------------
+
+# Both sides evaluate the K transform, the quantiser and the sums in fp64; only
+# the summation order differs.
+STAT_TOL = np.array([1e-9, 1e-11, 1e-11, 1e-13, 1e-11])
+
+
+def run_stats(w, k, pos, angles, b, g):
+    st = torch.empty(8, dtype=torch.float64, device=DEV)
+    rrp.quant_error_stats(shape_of(w), to_dev(k), to_dev(pos), support_b=b, group=g, stats_out=st,
+                          angles=None if angles is None else to_dev(angles))
+    torch.cuda.synchronize()
+    return st.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_quant_error_stats_parity_support_sweep(n):
+    w, inp = W.WORKLOADS[n], inputs(n)
+    _, phi32, _ = O.angles_from_moments(O.calibrate_moments(oshape_of(w), inp["q"], inp["k"], inp["pos"]),
+                                        O.EST_DEFAULT)
+    rows = []
+    for b, ang in [(bb, None) for bb in (1, 2, 4, 8, 16, 32, 64)] + [(1, phi32), (64, phi32)]:
+        g = run_stats(w, inp["k"], inp["pos"], ang, b, w.group)
+        r = O.quant_error_stats(oshape_of(w), inp["k"], inp["pos"], ang, b, w.group)
+        rel = np.abs(g[:5] - r[:5]) / np.maximum(np.abs(r[:5]), 1e-300)
+        assert np.all(rel <= STAT_TOL), (b, g, r, rel)
+        assert g[5] == r[5] and g[6] == r[6] and g[7] == 0
+        rows.append((b, ang is not None, math.sqrt(g[0] / g[1]), g[2] / g[5], g[3]))
+    print(f"workload {n}: (b, angles, rel_err, mean K range, max K range)")
+    for row in rows:
+        print("  ", row)
+
+
+def test_quant_error_stats_is_deterministic():
+    w, inp = W.WORKLOADS[3], inputs(3)
+    a = run_stats(w, inp["k"], inp["pos"], None, 128, 128)
+    b = run_stats(w, inp["k"], inp["pos"], None, 128, 128)
+    assert np.array_equal(a, b)

@@ -7,7 +7,10 @@ rotation by the calibrated angles, the block Hadamard, the Q store and the K
 group quantisation / nibble packing.  Inputs are resident in HBM before the
 timed region.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--hot-path-only]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 50] [--no-cpu-baseline] [--hot-path-only]
+
+A step takes about half a millisecond, so the defaults time about 0.1 s of
+launches after about 25 ms of warm-up launches (clocks settle).
 
 --hot-path-only skips the supporting passes, the decode timing and the CPU
 baseline (short runs under a profiler).  Every run also times a plain
@@ -66,7 +69,7 @@ def cpu_baseline(w, inp, angles_np, budget_s=12.0):
     t0 = time.perf_counter()
     O.rotate_quantize_qk(shp, inp["q"][:n], inp["k"][:n], inp["pos"][:n], angles_np, 128, 128)
     dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = O.max_threads()
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of {w.n_tokens} tokens, same inputs and angles, {dt:.1f} s"}
 
@@ -110,8 +113,8 @@ def decode_latency_us(dev, stream, reps=50):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hot-path-only", action="store_true")
     args = ap.parse_args()

@@ -61,6 +61,8 @@ def lib():
         L.orc_angles_from_moments.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.orc_quant_error_stats.argtypes = [
             ctypes.POINTER(Shape), ctypes.c_int, vp, vp, i64, vp, ctypes.c_int, ctypes.c_int, vp]
+        L.orc_max_threads.argtypes = []
+        L.orc_max_threads.restype = ctypes.c_int
         for name in ("orc_rotate_quantize_qk", "orc_calibrate_moments",
                      "orc_angles_from_moments", "orc_quant_error_stats"):
             getattr(L, name).restype = ctypes.c_int
@@ -159,6 +161,11 @@ def pack_nibbles(q):
 
 
 # ---- operations ------------------------------------------------------------
+
+def max_threads():
+    """OpenMP threads the token-parallel oracle functions use."""
+    return int(lib().orc_max_threads())
+
 
 def shape(n_q_heads, n_kv_heads, head_dim, rope_theta, rope_layout=HALF_SPLIT):
     return Shape(int(n_q_heads), int(n_kv_heads), int(head_dim), int(rope_layout), float(rope_theta))

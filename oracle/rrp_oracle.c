@@ -17,6 +17,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_MAX_DIM 1024
 
@@ -456,4 +459,14 @@ int orc_quant_error_stats(const orc_shape* s, int dtype, const void* k, const in
     stats[6] = n_rows;
     stats[7] = 0.0;
     return 0;
+}
+
+/* Threads the token loops above may use (1 without OpenMP). */
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -123,6 +123,9 @@ int orc_quant_error_stats(const orc_shape* s, int dtype, const void* k, const in
                           int64_t n_tokens, const float* angles, int support_b, int group,
                           double* stats);
 
+/* Threads the token-parallel entry points may use (OpenMP), 1 without OpenMP. */
+int orc_max_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -98,7 +98,7 @@ __device__ __forceinline__ void load_row_chunks(const unsigned char* __restrict_
 // Passes kept in flight per token: Q rows and K rows of one token for the
 // Llama / Mistral head counts (32 Q + 8 KV heads at 8 rows per pass).
 #ifndef RRP_DEPTH_Q
-#define RRP_DEPTH_Q 2
+#define RRP_DEPTH_Q 1
 #endif
 template <int R> struct Depth {
     static constexpr int Q = R >= 16 ? (RRP_DEPTH_Q + 1) / 2 : RRP_DEPTH_Q;

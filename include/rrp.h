@@ -138,7 +138,7 @@ int rrp_rotate_quantize_qk(const rrp_shape* shape, int32_t dtype, const void* q,
  *
  * q may be NULL (Q stream not accumulated); then estimator must be K_ONLY.
  * n_tokens == 0 only finalises (if angles_out != NULL).
- * Allocates a scratch buffer of at most 2 * 1024 * head_dim/2 * 5 doubles
+ * Allocates a scratch buffer of at most 4096 * head_dim/2 * 5 doubles
  * stream-ordered (hipMallocAsync / hipFreeAsync) on `stream`. */
 int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
                          const int32_t* pos, int64_t n_tokens, int32_t estimator,
@@ -154,7 +154,7 @@ int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const void* q, c
  *                            sum of group (max y - min y), n_groups, n_rows, 0 }
  * (overwritten).  Relative error = sqrt(E / N); mean K range = [2] / [5].
  * Reduced in a fixed order (bit-reproducible).  Allocates a stream-ordered
- * scratch buffer of at most 1024 * 8 doubles on `stream`. */
+ * scratch buffer of at most 4096 * 5 doubles on `stream`. */
 int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
                           int64_t n_tokens, const float* angles, int32_t support_b, int32_t group,
                           double* stats_out, void* stream);

@@ -2,12 +2,15 @@
 // heads and tokens, then the closed-form minimax-variance angle per pair.
 //
 // Blocks [0, nbq) accumulate the Q stream, blocks [nbq, nbq + nbk) the K
-// stream.  Each wave walks tokens with a fixed stride; every lane keeps fp64
-// sums for the CE pairs whose two channels it holds (n is known on the host).
-// A wave's row groups are folded with lane shuffles, the block's waves through
-// LDS, both in a fixed order; block partials go to a scratch array that a
-// single-block kernel sums in block order -- so the moments are bit-identical
-// from run to run.
+// stream.  A row of head_dim channels is held by P/4 lanes, each with four
+// RoPE pairs (two 8-byte loads for bf16, two 16-byte loads for fp32), so the
+// five fp64 sums per pair stay within a few dozen registers.  Each wave walks
+// tokens with a fixed stride and keeps the next group of row passes in flight
+// while it accumulates the current one.  A wave's row groups are folded with
+// lane shuffles, the block's waves through LDS, both in a fixed order; block
+// partials go to a scratch array laid out [pair * 5 + sum][block], which one
+// wave per (stream, pair, sum) reduces in a fixed order -- so the moments are
+// bit-identical from run to run.
 #include "rrp_device.hpp"
 #include "rrp_kernels.hpp"
 
@@ -16,21 +19,50 @@ namespace rrp {
 namespace {
 
 constexpr int kNSum = 5;  // sum u, sum v, sum u^2, sum v^2, sum u*v
+constexpr int kCP = 4;    // RoPE pairs per lane
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Four consecutive elements of one row.
+template <typename E> struct Quad;
+template <> struct Quad<bf16_tag> {
+    typedef u32x2 T;
+    __device__ static void unpack(const T& w, float (&x)[4]) {
+        x[0] = __uint_as_float(w.x << 16);
+        x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+        x[2] = __uint_as_float(w.y << 16);
+        x[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    }
+    __device__ static T zero() { return T{0u, 0u}; }
+};
+template <> struct Quad<float> {
+    typedef u32x4 T;
+    __device__ static void unpack(const T& w, float (&x)[4]) {
+        x[0] = __uint_as_float(w.x);
+        x[1] = __uint_as_float(w.y);
+        x[2] = __uint_as_float(w.z);
+        x[3] = __uint_as_float(w.w);
+    }
+    __device__ static T zero() { return T{0u, 0u, 0u, 0u}; }
+};
+
+// MAXP: row passes loaded per step (a step is double-buffered across tokens).
 template <typename E, int D, int LAYOUT, int MAXP>
 __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
-    using G = Geo<E, D>;
-    constexpr int CE = G::CE, P = G::P, L = G::L, R = G::R;
+    constexpr int P = D / 2;
+    constexpr int LP = P / kCP;  // lanes per row
+    constexpr int RP = 64 / LP;  // rows per pass
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr size_t ROWB = (size_t)D * EB;
+    using QT = typename Quad<E>::T;
     __shared__ double2 tab_all[4][P];
-    __shared__ double red[4][P][kNSum];
+    __shared__ double red[4][P * kNSum];
 
     const int lane = (int)__lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int nwave = (int)(blockDim.x >> 6);
-    const int s = lane & (L - 1);
-    const int grp = lane / L;
+    const int s = lane % LP;
+    const int grp = lane / LP;
     double2* tab = tab_all[wave];
 
     const bool is_k = (int)blockIdx.x >= a.nbq;
@@ -38,137 +70,157 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
     const int nb = is_k ? a.nbk : a.nbq;
     const unsigned char* src = static_cast<const unsigned char*>(is_k ? a.k : a.q);
     const int nh = is_k ? a.hk : a.hq;
-    const int npass = (nh + R - 1) / R;
+    const int npass = (nh + RP - 1) / RP;
+    const int nstep = (npass + MAXP - 1) / MAXP;
     const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
-    int kidx[CE];
-    pair_index_of_lane<D, LAYOUT, CE>(s, kidx);
+    // Element offsets of the lane's two quads: half-split pairs (k, k + P) for
+    // k in [4s, 4s + 4); interleaved pairs (2k, 2k + 1) for the same k.
+    const int off0 = LAYOUT == 0 ? s * kCP : 2 * s * kCP;
+    const int off1 = LAYOUT == 0 ? P + s * kCP : 2 * s * kCP + kCP;
 
-    double acc[CE][kNSum];
+    double acc[kCP][kNSum];
 #pragma unroll
-    for (int j = 0; j < CE; ++j)
+    for (int j = 0; j < kCP; ++j)
 #pragma unroll
         for (int m = 0; m < kNSum; ++m) acc[j][m] = 0.0;
 
-    for (int64_t t = (int64_t)bs * nwave + wave; t < a.n_tokens; t += (int64_t)nb * nwave) {
-        const int p = a.pos[t];
-        double c[CE], sn[CE];
-        for (int p0 = 0; p0 < npass; p0 += MAXP) {
-            u32x4 raw[MAXP][2];
+    const int64_t stride = (int64_t)nb * nwave;
+    auto load_step = [&](int64_t t, int st, QT (&raw)[MAXP][2]) {
 #pragma unroll
-            for (int i = 0; i < MAXP; ++i) {
-                const int row = (p0 + i) * R + grp;
-                if (p0 + i < npass && row < nh) {
-                    const unsigned char* rp = src + ((size_t)t * nh + row) * ROWB;
-#pragma unroll
-                    for (int ch = 0; ch < 2; ++ch)
-                        raw[i][ch] = __builtin_nontemporal_load(
-                            reinterpret_cast<const u32x4*>(rp + chunk_offset<E, D>(ch, s)));
-                } else {
-                    raw[i][0] = raw[i][1] = u32x4{0, 0, 0, 0};
-                }
-            }
-            if (p0 == 0) {
-                if (lane < P) {
-                    double sa, ca;
-                    sincos_f64_of_f32(rope_angle_f32(p, invf), sa, ca);
-                    tab[lane] = make_double2(ca, sa);
-                }
-                wave_lds_sync();
-#pragma unroll
-                for (int j = 0; j < CE; ++j) {
-                    const double2 v = tab[kidx[j]];
-                    c[j] = v.x;
-                    sn[j] = v.y;
-                }
-                wave_lds_sync();
-            }
-#pragma unroll
-            for (int i = 0; i < MAXP; ++i) {
-                const int row = (p0 + i) * R + grp;
-                if (!(p0 + i < npass)) break;
-                if (row >= nh) continue;
-                float x[2][CE];
-                unpack_chunk<E, CE>(raw[i][0], x[0]);
-                unpack_chunk<E, CE>(raw[i][1], x[1]);
-#pragma unroll
-                for (int j = 0; j < CE; ++j) {
-                    double xa, xb;
-                    if constexpr (LAYOUT == 0) {
-                        xa = x[0][j];
-                        xb = x[1][j];
-                    } else {
-                        const int ch = j / (CE / 2), i2 = 2 * (j % (CE / 2));
-                        xa = x[ch][i2];
-                        xb = x[ch][i2 + 1];
-                    }
-                    const double u = xa * c[j] - xb * sn[j];
-                    const double v = xb * c[j] + xa * sn[j];
-                    acc[j][0] += u;
-                    acc[j][1] += v;
-                    acc[j][2] += u * u;
-                    acc[j][3] += v * v;
-                    acc[j][4] += u * v;
-                }
+        for (int i = 0; i < MAXP; ++i) {
+            const int row = (st * MAXP + i) * RP + grp;
+            if (st * MAXP + i < npass && row < nh) {
+                const unsigned char* rp = src + ((size_t)t * nh + row) * ROWB;
+                raw[i][0] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(rp + off0 * EB));
+                raw[i][1] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(rp + off1 * EB));
+            } else {
+                raw[i][0] = raw[i][1] = Quad<E>::zero();
             }
         }
+    };
+
+    int64_t t = (int64_t)bs * nwave + wave;
+    int st = 0;
+    QT cur[MAXP][2], nxt[MAXP][2];
+    if (t < a.n_tokens) load_step(t, 0, cur);
+    double c[kCP], sn[kCP];
+    while (t < a.n_tokens) {
+        int64_t tn = t;
+        int sn_step = st + 1;
+        if (sn_step == nstep) {
+            tn = t + stride;
+            sn_step = 0;
+        }
+        if (tn < a.n_tokens) load_step(tn, sn_step, nxt);
+        if (st == 0) {
+            const int p = a.pos[t];
+            wave_lds_sync();  // previous token's table reads are complete
+            if (lane < P) {
+                double sa, ca;
+                sincos_f64_of_f32(rope_angle_f32(p, invf), sa, ca);
+                tab[lane] = make_double2(ca, sa);
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int j = 0; j < kCP; ++j) {
+                const double2 v = tab[s * kCP + j];
+                c[j] = v.x;
+                sn[j] = v.y;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            const int row = (st * MAXP + i) * RP + grp;
+            if (!(st * MAXP + i < npass && row < nh)) continue;
+            float x0[4], x1[4];
+            Quad<E>::unpack(cur[i][0], x0);
+            Quad<E>::unpack(cur[i][1], x1);
+#pragma unroll
+            for (int j = 0; j < kCP; ++j) {
+                double xa, xb;
+                if constexpr (LAYOUT == 0) {
+                    xa = x0[j];
+                    xb = x1[j];
+                } else if (j < kCP / 2) {
+                    xa = x0[2 * j];
+                    xb = x0[2 * j + 1];
+                } else {
+                    xa = x1[2 * (j - kCP / 2)];
+                    xb = x1[2 * (j - kCP / 2) + 1];
+                }
+                const double u = xa * c[j] - xb * sn[j];
+                const double v = xb * c[j] + xa * sn[j];
+                acc[j][0] += u;
+                acc[j][1] += v;
+                acc[j][2] += u * u;
+                acc[j][3] += v * v;
+                acc[j][4] += u * v;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            cur[i][0] = nxt[i][0];
+            cur[i][1] = nxt[i][1];
+        }
+        t = tn;
+        st = sn_step;
     }
 
-    // Fold the wave's R row groups (lanes s, s + L, s + 2L, ...) in a fixed order.
+    // Fold the wave's row groups (lanes s, s + LP, s + 2 LP, ...) in a fixed order.
 #pragma unroll
-    for (int m = L; m < 64; m <<= 1)
+    for (int m = LP; m < 64; m <<= 1)
 #pragma unroll
-        for (int j = 0; j < CE; ++j)
+        for (int j = 0; j < kCP; ++j)
 #pragma unroll
             for (int q = 0; q < kNSum; ++q) acc[j][q] += shfl_xor_d(acc[j][q], m);
     if (grp == 0) {
 #pragma unroll
-        for (int j = 0; j < CE; ++j)
+        for (int j = 0; j < kCP; ++j)
 #pragma unroll
-            for (int q = 0; q < kNSum; ++q) red[wave][kidx[j]][q] = acc[j][q];
+            for (int q = 0; q < kNSum; ++q) red[wave][(s * kCP + j) * kNSum + q] = acc[j][q];
     }
     __syncthreads();
+    const int nbt = a.nbq + a.nbk;
     for (int e = (int)threadIdx.x; e < P * kNSum; e += (int)blockDim.x) {
         double sum = 0.0;
-        for (int w = 0; w < nwave; ++w) sum += (&red[w][0][0])[e];
-        a.partials[(size_t)blockIdx.x * P * kNSum + e] = sum;
+        for (int w = 0; w < nwave; ++w) sum += red[w][e];
+        a.partials[(size_t)e * nbt + blockIdx.x] = sum;
     }
 }
 
-// One block: 2 * P * 5 threads sum the block partials of their (stream, pair,
-// sum) in block order, add them to the caller's moments, then P threads
-// finalise the angles from the accumulated moments.
-__global__ __launch_bounds__(1024) void calib_final_kernel(const CalibFinalArgs a) {
-    __shared__ double M[2][kMaxPairs][6];
+// One wave per (stream, pair, sum): lane l adds the partials of blocks l, l + 64,
+// ... in order, then the wave folds its lanes with a fixed xor butterfly (every
+// lane ends with the same value), and lane 0 adds it to the caller's moments.
+__global__ __launch_bounds__(256) void calib_reduce_kernel(const CalibFinalArgs a) {
     const int P = a.n_pairs;
-    const int tid = (int)threadIdx.x;
-    if (tid < 2 * P * kNSum) {
-        const int stream = tid / (P * kNSum);
-        const int rem = tid % (P * kNSum);
-        const int k = rem / kNSum, j = rem % kNSum;
-        const int b0 = stream ? a.nbq : 0;
-        const int nb = stream ? a.nbk : a.nbq;
+    const int w = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (w >= 2 * P * kNSum) return;  // uniform per wave
+    const int lane = (int)__lane_id();
+    const int stream = w / (P * kNSum);
+    const int e = w % (P * kNSum);  // pair * 5 + sum
+    const int k = e / kNSum, j = e % kNSum;
+    const int b0 = stream ? a.nbq : 0;
+    const int nb = stream ? a.nbk : a.nbq;
+    if (nb == 0) return;  // stream not accumulated by this call
+    const int nbt = a.nbq + a.nbk;
+    const double* part = a.partials + (size_t)e * nbt + b0;
+    double sum = 0.0;
+    for (int b = lane; b < nb; b += 64) sum += part[b];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) sum += shfl_xor_d(sum, m);
+    if (lane == 0) {
         double* mom = a.moments + ((size_t)k * 2 + stream) * 6;
-        double val = mom[1 + j];
-        if (nb > 0) {
-            double sum = 0.0;
-            for (int b = 0; b < nb; ++b) sum += a.partials[((size_t)(b0 + b) * P + k) * kNSum + j];
-            val += sum;
-            mom[1 + j] = val;
-        }
-        M[stream][k][1 + j] = val;
-        if (j == 0) {
-            double n = mom[0];
-            if (nb > 0) {
-                n += stream ? a.n_rows_k : a.n_rows_q;
-                mom[0] = n;
-            }
-            M[stream][k][0] = n;
-        }
+        mom[1 + j] += sum;
+        if (j == 0) mom[0] += stream ? a.n_rows_k : a.n_rows_q;
     }
-    __syncthreads();
-    if (a.angles_out == nullptr || tid >= P) return;
-    const double* mq = M[0][tid];
-    const double* mk = M[1][tid];
+}
+
+// One thread per pair: estimator, centred covariance, phi* wrapped to (-pi/4, pi/4].
+__global__ __launch_bounds__(64) void calib_angles_kernel(const CalibFinalArgs a) {
+    const int k = (int)threadIdx.x;
+    if (k >= a.n_pairs) return;
+    const double* mq = a.moments + (size_t)k * 12;
+    const double* mk = mq + 6;
     const bool use_q = a.estimator != 1 && mq[0] > 0.0;
     const bool use_k = mk[0] > 0.0;
     double n = 0.0, E[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
@@ -198,25 +250,28 @@ __global__ __launch_bounds__(1024) void calib_final_kernel(const CalibFinalArgs 
         if (phi > quarter_pi) phi -= 2.0 * quarter_pi;
         if (phi <= -quarter_pi) phi += 2.0 * quarter_pi;
     }
-    a.angles_out[tid] = (float)phi;
+    a.angles_out[k] = (float)phi;
 }
+
+#ifndef RRP_CALIB_MAXP
+#define RRP_CALIB_MAXP 2
+#endif
 
 template <typename E, int D, int LAYOUT>
 hipError_t launch_t(const CalibArgs& a, hipStream_t st) {
-    constexpr int MAXP = 4;
     const int blocks = a.nbq + a.nbk;
-    hipLaunchKernelGGL((calib_moments_kernel<E, D, LAYOUT, MAXP>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((calib_moments_kernel<E, D, LAYOUT, RRP_CALIB_MAXP>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int* nbq, int* nbk) {
-    // About 8 tokens per wave per stream, at most kMaxReduceBlocks blocks, split
+    // About 8 tokens per wave per stream, at most kMaxCalibBlocks blocks, split
     // between the streams in proportion to their rows.
     int64_t want = (n_tokens * (with_q ? 2 : 1) + 31) / 32;
     if (want < (with_q ? 2 : 1)) want = with_q ? 2 : 1;
-    if (want > kMaxReduceBlocks) want = kMaxReduceBlocks;
+    if (want > kMaxCalibBlocks) want = kMaxCalibBlocks;
     const int total = (int)want;
     if (!with_q || hq == 0) {
         *nbq = 0;
@@ -246,8 +301,14 @@ hipError_t launch_calibrate(const CalibArgs& a, int dtype, int head_dim, int lay
 }
 
 hipError_t launch_calibrate_final(const CalibFinalArgs& a, hipStream_t st) {
-    const int threads = ((2 * a.n_pairs * kNSum + 63) / 64) * 64;
-    hipLaunchKernelGGL(calib_final_kernel, dim3(1), dim3(threads), 0, st, a);
+    if (a.nbq + a.nbk > 0) {
+        const int waves = 2 * a.n_pairs * kNSum;
+        hipLaunchKernelGGL(calib_reduce_kernel, dim3((waves + 3) / 4), dim3(256), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.angles_out == nullptr) return hipSuccess;
+    hipLaunchKernelGGL(calib_angles_kernel, dim3(1), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 

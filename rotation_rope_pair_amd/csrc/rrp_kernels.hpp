@@ -7,7 +7,8 @@
 namespace rrp {
 
 constexpr int kMaxPairs = 64;        // head_dim <= 128
-constexpr int kMaxReduceBlocks = 1024;
+constexpr int kMaxCalibBlocks = 4096;  // block partials of the calibration pass
+constexpr int kMaxStatsBlocks = 4096;  // block partials of the diagnostic pass
 
 // RoPE frequencies travel in the kernel argument block: every lane reads its
 // own pair's entry, so no device table has to be allocated or kept.
@@ -38,7 +39,7 @@ struct CalibArgs {
     const void* q;
     const void* k;
     const int32_t* pos;
-    double* partials;  // [n_blocks][P][5]
+    double* partials;  // [P * 5][n_blocks]
     int64_t n_tokens;
     int32_t hq;
     int32_t hk;
@@ -63,7 +64,7 @@ struct StatsArgs {
     const void* k;
     const int32_t* pos;
     const float* angles;
-    double* partials;  // [n_blocks][5]
+    double* partials;  // [5][n_blocks]
     int64_t n_tokens;
     int32_t hk;
     int32_t support_b;

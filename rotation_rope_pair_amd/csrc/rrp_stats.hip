@@ -15,7 +15,8 @@ namespace {
 
 constexpr int kNStat = 5;  // E, N, sum absmax, max absmax, sum range
 
-template <typename E, int D, int LAYOUT, int MAXP, int BT>
+// SMALLG: groups smaller than one 16-byte chunk (reduced in registers).
+template <typename E, int D, int LAYOUT, int BT, bool SMALLG>
 __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     using G = Geo<E, D>;
     using LM = LaneMap<G::L>;
@@ -44,92 +45,101 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     const unsigned char* kb = static_cast<const unsigned char*>(a.k);
     const int npass = (a.hk + R - 1) / R;
     const int g = a.group;
+    const int64_t stride = (int64_t)gridDim.x * nwave;
+
+    auto load_pass = [&](int64_t t, int ps, u32x4 (&raw)[2]) {
+        const int row = ps * R + grp;
+        if (row < a.hk) {
+            const unsigned char* rp = kb + ((size_t)t * a.hk + row) * ROWB;
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch)
+                raw[ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + chunk_offset<E, D>(ch, s_src)));
+        } else {
+            raw[0] = raw[1] = u32x4{0, 0, 0, 0};
+        }
+    };
 
     double accE = 0.0, accN = 0.0, accM = 0.0, maxM = 0.0, accR = 0.0;
-    for (int64_t t = (int64_t)blockIdx.x * nwave + wave; t < a.n_tokens; t += (int64_t)gridDim.x * nwave) {
-        const int p = a.pos[t];
-        for (int p0 = 0; p0 < npass; p0 += MAXP) {
-            u32x4 raw[MAXP][2];
+    int64_t t = (int64_t)blockIdx.x * nwave + wave;
+    int ps = 0;
+    u32x4 cur[2], nxt[2];
+    if (t < a.n_tokens) load_pass(t, 0, cur);
+    while (t < a.n_tokens) {
+        // keep the next pass (this token's or the next token's first) in flight
+        int64_t tn = t;
+        int pn = ps + 1;
+        if (pn == npass) {
+            tn = t + stride;
+            pn = 0;
+        }
+        if (tn < a.n_tokens) load_pass(tn, pn, nxt);
+        if (ps == 0) token_tables<D, FOLD>(tab32, tab64, lane, a.pos[t], invf, cphi, sphi, a.rsqrt_b);
+        if (ps * R + grp < a.hk) {
+            float yf[2][CE];
+            unpack_chunk<E, CE>(cur[0], yf[0]);
+            unpack_chunk<E, CE>(cur[1], yf[1]);
+            double y[2][CE];
 #pragma unroll
-            for (int i = 0; i < MAXP; ++i) {
-                const int row = (p0 + i) * R + grp;
-                if (p0 + i < npass && row < a.hk) {
-                    const unsigned char* rp = kb + ((size_t)t * a.hk + row) * ROWB;
+            for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-                    for (int ch = 0; ch < 2; ++ch)
-                        raw[i][ch] = __builtin_nontemporal_load(
-                            reinterpret_cast<const u32x4*>(rp + chunk_offset<E, D>(ch, s_src)));
-                } else {
-                    raw[i][0] = raw[i][1] = u32x4{0, 0, 0, 0};
-                }
-            }
-            if (p0 == 0) token_tables<D, FOLD>(tab32, tab64, lane, p, invf, cphi, sphi, a.rsqrt_b);
+                for (int i2 = 0; i2 < CE; ++i2) y[ch][i2] = (double)yf[ch][i2];
+            rotate_lds<LAYOUT, FOLD>(y, tab64, kidx);
+            fwht_row<D, CE, BT, FOLD>(y, a.support_b, s);
+            if constexpr (!SMALLG) {
+                // one group value per chunk: absmax, max, min over the group
+                double ca[2], cx[2], cn[2];
 #pragma unroll
-            for (int i = 0; i < MAXP; ++i) {
-                const int row = (p0 + i) * R + grp;
-                if (!(p0 + i < npass)) break;
-                if (row >= a.hk) continue;
-                float yf[2][CE];
-                unpack_chunk<E, CE>(raw[i][0], yf[0]);
-                unpack_chunk<E, CE>(raw[i][1], yf[1]);
-                double y[2][CE];
+                for (int ch = 0; ch < 2; ++ch) {
+                    ca[ch] = 0.0;
+                    cx[ch] = y[ch][0];
+                    cn[ch] = y[ch][0];
 #pragma unroll
-                for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-                    for (int i2 = 0; i2 < CE; ++i2) y[ch][i2] = (double)yf[ch][i2];
-                rotate_lds<LAYOUT, FOLD>(y, tab64, kidx);
-                fwht_row<D, CE, BT, FOLD>(y, a.support_b, s);
-                // Per-value group reductions: absmax, max, min.
-                double am[2][CE], mx[2][CE], mn[2][CE];
-                if (g >= CE) {
-                    double ca[2], cx[2], cn[2];
-#pragma unroll
-                    for (int ch = 0; ch < 2; ++ch) {
-                        ca[ch] = 0.0;
-                        cx[ch] = y[ch][0];
-                        cn[ch] = y[ch][0];
-#pragma unroll
-                        for (int i2 = 0; i2 < CE; ++i2) {
-                            ca[ch] = fmax(ca[ch], fabs(y[ch][i2]));
-                            cx[ch] = fmax(cx[ch], y[ch][i2]);
-                            cn[ch] = fmin(cn[ch], y[ch][i2]);
-                        }
+                    for (int i2 = 0; i2 < CE; ++i2) {
+                        ca[ch] = fmax(ca[ch], fabs(y[ch][i2]));
+                        cx[ch] = fmax(cx[ch], y[ch][i2]);
+                        cn[ch] = fmin(cn[ch], y[ch][i2]);
                     }
-                    group_reduce_chunkwise<D, CE, true>(ca, g);
-                    group_reduce_chunkwise<D, CE, true>(cx, g);
-                    group_reduce_chunkwise<D, CE, false>(cn, g);
-#pragma unroll
-                    for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-                        for (int i2 = 0; i2 < CE; ++i2) {
-                            am[ch][i2] = ca[ch];
-                            mx[ch][i2] = cx[ch];
-                            mn[ch][i2] = cn[ch];
-                        }
-                } else {
-#pragma unroll
-                    for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-                        for (int i2 = 0; i2 < CE; ++i2) {
-                            am[ch][i2] = fabs(y[ch][i2]);
-                            mx[ch][i2] = y[ch][i2];
-                            mn[ch][i2] = y[ch][i2];
-                        }
-                    group_reduce_inreg<CE, true>(am, g);
-                    group_reduce_inreg<CE, true>(mx, g);
-                    group_reduce_inreg<CE, false>(mn, g);
                 }
+                group_reduce_chunkwise<D, CE, true>(ca, g);
+                group_reduce_chunkwise<D, CE, true>(cx, g);
+                group_reduce_chunkwise<D, CE, false>(cn, g);
+#pragma unroll
+                for (int ch = 0; ch < 2; ++ch) {
+                    const GroupScale64 gs = group_scale64(ca[ch]);
+#pragma unroll
+                    for (int i2 = 0; i2 < CE; ++i2) {
+                        const double diff = (double)code_of(y[ch][i2], gs.rcp) * gs.shv - y[ch][i2];
+                        accE += diff * diff;
+                        accN += y[ch][i2] * y[ch][i2];
+                    }
+                    if (((ch * P + s * CE) & (g - 1)) == 0) {  // the lane holding the group's first channel
+                        accM += ca[ch];
+                        maxM = fmax(maxM, ca[ch]);
+                        accR += cx[ch] - cn[ch];
+                    }
+                }
+            } else {
+                double am[2][CE], mx[2][CE], mn[2][CE];
 #pragma unroll
                 for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                     for (int i2 = 0; i2 < CE; ++i2) {
-                        const bool leader = (g >= CE) ? (i2 == 0 && ((ch * P + s * CE) & (g - 1)) == 0)
-                                                      : ((i2 & (g - 1)) == 0);
+                        am[ch][i2] = fabs(y[ch][i2]);
+                        mx[ch][i2] = y[ch][i2];
+                        mn[ch][i2] = y[ch][i2];
+                    }
+                group_reduce_inreg<CE, true>(am, g);
+                group_reduce_inreg<CE, true>(mx, g);
+                group_reduce_inreg<CE, false>(mn, g);
+#pragma unroll
+                for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                    for (int i2 = 0; i2 < CE; ++i2) {
                         const GroupScale64 gs = group_scale64(am[ch][i2]);
                         const double diff = (double)code_of(y[ch][i2], gs.rcp) * gs.shv - y[ch][i2];
                         accE += diff * diff;
                         accN += y[ch][i2] * y[ch][i2];
-                        if (leader) {
+                        if ((i2 & (g - 1)) == 0) {
                             accM += am[ch][i2];
                             maxM = fmax(maxM, am[ch][i2]);
                             accR += mx[ch][i2] - mn[ch][i2];
@@ -137,6 +147,10 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
                     }
             }
         }
+        cur[0] = nxt[0];
+        cur[1] = nxt[1];
+        t = tn;
+        ps = pn;
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
@@ -158,35 +172,45 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
         const int e = (int)threadIdx.x;
         double v = red[0][e];
         for (int w = 1; w < nwave; ++w) v = (e == 3) ? fmax(v, red[w][e]) : v + red[w][e];
-        a.partials[(size_t)blockIdx.x * kNStat + e] = v;
+        a.partials[(size_t)e * gridDim.x + blockIdx.x] = v;
     }
 }
 
-__global__ void stats_final_kernel(const StatsFinalArgs a) {
-    const int e = (int)threadIdx.x;
+// One wave per statistic: lane l combines the partials of blocks l, l + 64, ...
+// in order, then a fixed xor butterfly folds the lanes (every lane ends with
+// the same value).  Partials are laid out [statistic][block].
+__global__ __launch_bounds__(512) void stats_final_kernel(const StatsFinalArgs a) {
+    const int e = (int)(threadIdx.x >> 6);
+    const int lane = (int)__lane_id();
     if (e < kNStat) {
+        const double* part = a.partials + (size_t)e * a.n_blocks;
         double v = 0.0;
-        for (int b = 0; b < a.n_blocks; ++b) {
-            const double x = a.partials[(size_t)b * kNStat + e];
-            v = (e == 3) ? fmax(v, x) : v + x;
+        for (int b = lane; b < a.n_blocks; b += 64) v = (e == 3) ? fmax(v, part[b]) : v + part[b];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const double o = shfl_xor_d(v, m);
+            v = (e == 3) ? fmax(v, o) : v + o;
         }
-        a.stats_out[e] = v;
-    } else if (e == 5) {
+        if (lane == 0) a.stats_out[e] = v;
+    } else if (e == kNStat && lane == 0) {
         a.stats_out[5] = a.n_groups;
-    } else if (e == 6) {
         a.stats_out[6] = a.n_rows;
-    } else if (e == 7) {
         a.stats_out[7] = 0.0;
     }
 }
 
 template <typename E, int D, int LAYOUT>
 hipError_t launch_t(const StatsArgs& a, int n_blocks, hipStream_t st) {
-    constexpr int MAXP = 1;
-    if (a.support_b == D)
-        hipLaunchKernelGGL((stats_kernel<E, D, LAYOUT, MAXP, D>), dim3(n_blocks), dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL((stats_kernel<E, D, LAYOUT, MAXP, 0>), dim3(n_blocks), dim3(256), 0, st, a);
+    constexpr int CE = Geo<E, D>::CE;
+    const bool small = a.group < CE;
+#define RRP_LAUNCH(BT, SG) \
+    hipLaunchKernelGGL((stats_kernel<E, D, LAYOUT, BT, SG>), dim3(n_blocks), dim3(256), 0, st, a)
+    if (a.support_b == D) {
+        if (small) RRP_LAUNCH(D, true); else RRP_LAUNCH(D, false);
+    } else {
+        if (small) RRP_LAUNCH(0, true); else RRP_LAUNCH(0, false);
+    }
+#undef RRP_LAUNCH
     return hipGetLastError();
 }
 
@@ -195,7 +219,7 @@ hipError_t launch_t(const StatsArgs& a, int n_blocks, hipStream_t st) {
 int stats_blocks(int64_t n_tokens) {
     int64_t b = (n_tokens + 15) / 16;  // about 4 tokens per wave
     if (b < 1) b = 1;
-    if (b > kMaxReduceBlocks) b = kMaxReduceBlocks;
+    if (b > kMaxStatsBlocks) b = kMaxStatsBlocks;
     return (int)b;
 }
 
@@ -214,7 +238,7 @@ hipError_t launch_stats(const StatsArgs& a, int n_blocks, int dtype, int head_di
 }
 
 hipError_t launch_stats_final(const StatsFinalArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(64 * (kNStat + 1)), 0, st, a);
     return hipGetLastError();
 }
 

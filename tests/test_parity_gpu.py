@@ -183,6 +183,23 @@ def test_rotate_parity_prefill_128k_bench_launch():
     print(rep)
 
 
+def test_rotate_parity_prefill_128k_every_token():
+    """The same benchmark launch compared element by element on all 131072 tokens
+    (Q output bits, K codes and fp16 scales), in chunks the oracle runs in about a
+    second each."""
+    w, inp = W.WORKLOADS[4], inputs(4)
+    ang = random_angles(w.n_pairs, 114)
+    out = run_rotate(w, inp, ang, 128, 128, debug=False)
+    totals = {"rows": 0, "scale_mismatch": 0, "scale_band": 0, "code_mismatch": 0, "code_band": 0}
+    chunk = 16384
+    for t0 in range(0, w.n_tokens, chunk):
+        rep = check_rotate(w, inp, out, ang, 128, 128, np.arange(t0, min(w.n_tokens, t0 + chunk)))
+        for key in totals:
+            totals[key] += rep[key]
+    assert totals["rows"] == w.n_tokens * w.n_kv_heads
+    print(totals)
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("n", [1, 2, 3])
 def test_rotate_parity_rope_layouts(n, layout):

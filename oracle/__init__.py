@@ -61,6 +61,9 @@ def lib():
         L.orc_angles_from_moments.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.orc_quant_error_stats.argtypes = [
             ctypes.POINTER(Shape), ctypes.c_int, vp, vp, i64, vp, ctypes.c_int, ctypes.c_int, vp]
+        L.orc_quantize_v.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, vp, i64, ctypes.c_int, vp, vp, vp, i64,
+                                     vp, vp]
+        L.orc_quantize_v.restype = ctypes.c_int
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = ctypes.c_int
         for name in ("orc_rotate_quantize_qk", "orc_calibrate_moments",
@@ -200,6 +203,28 @@ def rotate_quantize_qk(shp, q, k, pos, angles, support_b, group, slot_mapping=No
         _p(out["q_rot"]), _p(out["k_rot"]), _p(out["k_scale32"]))
     if rc != 0:
         raise ValueError("oracle rotate_quantize_qk rejected its arguments")
+    return out
+
+
+def quantize_v(shp, v, group, slot_mapping=None, n_slots=None):
+    """V half of the KV4 cache.  Returns a dict with v_rot (fp64 [T][Hkv][d]),
+    v_codes (uint8 [n_slots][Hkv][d/2]), v_scales (fp16 bits), v_scale32 (fp32)."""
+    va, dt = _in(v)
+    T = va.shape[0]
+    d, hk = shp.head_dim, shp.n_kv_heads
+    if n_slots is None:
+        n_slots = T if slot_mapping is None else int(np.max(slot_mapping, initial=-1)) + 1
+    sm = None if slot_mapping is None else _c(slot_mapping, np.int64)
+    out = {
+        "v_rot": np.zeros((T, hk, d), np.float64),
+        "v_codes": np.zeros((n_slots, hk, d // 2), np.uint8),
+        "v_scales": np.zeros((n_slots, hk, d // group), np.uint16),
+        "v_scale32": np.zeros((T, hk, d // group), np.float32),
+    }
+    rc = lib().orc_quantize_v(ctypes.byref(shp), dt, _p(va), T, int(group), _p(out["v_codes"]),
+                              _p(out["v_scales"]), _p(sm), int(n_slots), _p(out["v_rot"]), _p(out["v_scale32"]))
+    if rc != 0:
+        raise ValueError("oracle quantize_v rejected its arguments")
     return out
 
 

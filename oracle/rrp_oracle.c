@@ -312,6 +312,44 @@ int orc_rotate_quantize_qk(const orc_shape* s, int dtype, const void* q, const v
     return 0;
 }
 
+/* V side of the KV4 cache ([NOTES] section 3.2.2: V is multiplied online by the
+ * head-wise Hadamard so the value cache loses its outliers; the Hadamard left on
+ * the attention output folds into the output projection offline).  No RoPE and
+ * no pair rotation: y = H_d / sqrt(d) . v, then the K quantiser and packing. */
+int orc_quantize_v(const orc_shape* s, int dtype, const void* v, int64_t n_tokens, int group,
+                   uint8_t* v_codes, uint16_t* v_scales, const int64_t* slot_mapping, int64_t n_slots,
+                   double* v_rot, float* v_scale32)
+{
+    if (check_shape(s) || n_tokens < 0 || !v || !v_codes || !v_scales) return -1;
+    const int d = s->head_dim, hk = s->n_kv_heads;
+    if (group < 2 || (group & 1) || d % group) return -1;
+    const int ng = d / group;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_tokens; ++t) {
+        double x[ORC_MAX_DIM], y[ORC_MAX_DIM];
+        int8_t codes[ORC_MAX_DIM];
+        const int64_t slot = slot_mapping ? slot_mapping[t] : t;
+        const int in_cache = slot >= 0 && slot < n_slots;
+        for (int h = 0; h < hk; ++h) {
+            const int64_t row = (t * hk + h) * (int64_t)d;
+            for (int c = 0; c < d; ++c) x[c] = load_elem(v, dtype, row + c);
+            orc_hadamard_blocks(x, d, d, y);
+            if (v_rot)
+                for (int c = 0; c < d; ++c) v_rot[row + c] = y[c];
+            for (int j = 0; j < ng; ++j) {
+                uint16_t sh;
+                float s32;
+                orc_quantize_group(y + j * group, group, codes + j * group, &sh, &s32);
+                if (v_scale32) v_scale32[(t * hk + h) * ng + j] = s32;
+                if (in_cache) v_scales[(slot * hk + h) * ng + j] = sh;
+            }
+            if (in_cache) orc_pack_nibbles(codes, d, v_codes + (slot * hk + h) * (int64_t)(d / 2));
+        }
+    }
+    return 0;
+}
+
 /* Calibration sums ([RAQK] estimator strategies: raw Q and K moment accumulators
  * pooled across heads before centring; optimisation objective: pooled-covariance,
  * position-averaged surrogate).  The samples are the post-RoPE pairs of every

@@ -107,6 +107,14 @@ int orc_rotate_quantize_qk(const orc_shape* s, int dtype, const void* q, const v
                            uint16_t* k_scales, const int64_t* slot_mapping, int64_t n_slots,
                            double* q_rot, double* k_rot, float* k_scale32);
 
+/* Quantise V rows into the V half of the KV4 cache: y = H_d / sqrt(d) . v (full-head
+ * Sylvester Hadamard, no RoPE, no pair rotation), then the K group quantiser and
+ * packing.  v: [T][Hkv][d]; v_codes / v_scales / slot rules as for K;
+ * v_rot (may be NULL): fp64 [T][Hkv][d]; v_scale32 (may be NULL): fp32 [T][Hkv][d/g]. */
+int orc_quantize_v(const orc_shape* s, int dtype, const void* v, int64_t n_tokens, int group,
+                   uint8_t* v_codes, uint16_t* v_scales, const int64_t* slot_mapping, int64_t n_slots,
+                   double* v_rot, float* v_scale32);
+
 /* Accumulate post-RoPE pair moments into moments[P][2][6] (n, Su, Sv, Suu, Svv, Suv);
  * q may be NULL (Q stream skipped). */
 int orc_calibrate_moments(const orc_shape* s, int dtype, const void* q, const void* k,

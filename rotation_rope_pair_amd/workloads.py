@@ -14,7 +14,8 @@ Every random stream is numpy PCG64 seeded by a SeedSequence of
 (1000 + workload number, stream id[, chunk index]): stream 0 draws the
 per-(stream, head, channel) parameters (Q heads first, then K heads),
 stream 1 the decode positions, streams 2 / 3 the Q / K samples of the
-evaluated batch and 4 / 5 those of the calibration batch, one generator per
+evaluated batch and 4 / 5 those of the calibration batch, stream 7 the V
+parameters (K's recipe, own draw) and stream 6 the V samples, one generator per
 chunk of 4096 tokens (so any token prefix draws identical bytes).  Values are
 generated in fp32 and, for bf16 workloads, rounded to bf16 (nearest-even) by
 torch; the same bytes feed the GPU path and the oracle.
@@ -60,14 +61,16 @@ class Workload:
     def elem_bytes(self):
         return 4 if self.dtype == "f32" else 2
 
-    def bytes_per_token(self, group=None, with_slot=None):
+    def bytes_per_token(self, group=None, with_slot=None, with_v=False):
         """Algorithmic HBM bytes one rotate+quantise launch must move per token:
-        Q read + K read + Q write + K codes + K fp16 scales + position (+ slot)."""
+        Q read + K read + Q write + K codes + K fp16 scales + position (+ slot),
+        plus V read + V codes + V scales when the V side is written too."""
         g = group or self.group
         e = self.elem_bytes
         d, hq, hk = self.head_dim, self.n_q_heads, self.n_kv_heads
         slot = self.decode_positions > 0 if with_slot is None else with_slot
-        return hq * d * e * 2 + hk * d * e + hk * d // 2 + 2 * hk * (d // g) + 4 + (8 if slot else 0)
+        kv = hk * d * e + hk * d // 2 + 2 * hk * (d // g)
+        return hq * d * e * 2 + kv * (2 if with_v else 1) + 4 + (8 if slot else 0)
 
 
 WORKLOADS = {
@@ -145,10 +148,11 @@ def positions(w: Workload, n_tokens: int, rng=None) -> np.ndarray:
     return (np.arange(n_tokens, dtype=np.int64) % L).astype(np.int32)
 
 
-def make_inputs(number: int, n_tokens: Optional[int] = None, want_q: bool = True):
-    """Inputs of workload `number`: dict(q, k, pos, slot_mapping, n_slots, calib).
+def make_inputs(number: int, n_tokens: Optional[int] = None, want_q: bool = True, want_v: bool = False):
+    """Inputs of workload `number`: dict(q, k, v, pos, slot_mapping, n_slots, calib).
 
-    q: [T][Hq][d], k: [T][Hkv][d] as fp32 or bf16 bits; pos: int32[T];
+    q: [T][Hq][d], k and v: [T][Hkv][d] as fp32 or bf16 bits (v None unless
+    want_v); pos: int32[T];
     slot_mapping: int64[T] or None (identity); calib: same dict for the
     separate calibration batch (decode workload) or None."""
     w = WORKLOADS[number]
@@ -169,6 +173,7 @@ def make_inputs(number: int, n_tokens: Optional[int] = None, want_q: bool = True
     res["pos"] = pos
     res["q"] = _draw_samples((seed, 2), w, pq, T) if want_q else None
     res["k"] = _draw_samples((seed, 3), w, pk, T)
+    res["v"] = _draw_samples((seed, 6), w, _draw_params(_rng(seed, 7), w, w.n_kv_heads), T) if want_v else None
     res["calib"] = None
     if w.calib_tokens:
         Tc = w.calib_tokens

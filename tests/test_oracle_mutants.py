@@ -33,6 +33,9 @@ MUTANTS = {
     "pair_rotation_dropped": ("orc_hadamard_blocks(p, head_dim, b, out);", "orc_hadamard_blocks(r, head_dim, b, out); (void)p;"),
     "f16_round_half_up": ("return rint(a / quantum) * quantum;", "return trunc(a / quantum + 0.5) * quantum;"),
     "stats_range_max_only": ("sum_range += hi - lo;", "sum_range += hi;"),
+    "v_half_head_hadamard": ("orc_hadamard_blocks(x, d, d, y);", "orc_hadamard_blocks(x, d, d / 2, y);"),
+    "v_scale_at_token_not_slot": ("if (in_cache) v_scales[(slot * hk + h) * ng + j] = sh;",
+                                  "if (in_cache) v_scales[(t * hk + h) * ng + j] = sh;"),
 }
 
 

@@ -621,3 +621,81 @@ def test_transform_matches_complex_rotation_then_scipy_hadamard(orc, layout, b):
     H = scipy.linalg.hadamard(b).astype(np.float64) / math.sqrt(b)
     ref = (r.reshape(-1, b) @ H.T).reshape(-1)
     assert np.allclose(orc.transform_row(x, layout, inv, p, phi, b), ref, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# V side of the KV4 cache ([NOTES] section 3.2.2: V times the head-wise
+# Hadamard online; the Hadamard left on the attention output folds into W_O).
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,g", [(64, 64), (128, 128), (128, 8), (64, 2)])
+def test_v_transform_is_scipy_hadamard_and_codes_bound_the_error(orc, d, g):
+    from scipy.linalg import hadamard
+    rng = _rng(40 + d + g)
+    T, hk = 5, 3
+    v = (rng.standard_normal((T, hk, d)) * rng.lognormal(0, 1, d)).astype(np.float32)
+    v[1, 2, 7] = 300.0                                   # an outlier channel
+    out = orc.quantize_v(orc.shape(4, hk, d, 5e5), v, g)
+    H = hadamard(d).astype(np.float64) / math.sqrt(d)
+    ref = v.astype(np.float64) @ H.T
+    assert np.max(np.abs(out["v_rot"] - ref)) <= 1e-12 * np.max(np.abs(ref))
+    codes = _unpack(out["v_codes"]).astype(np.float64)
+    s = out["v_scales"].view(np.float16).astype(np.float64)
+    yhat = codes * np.repeat(s, g, axis=-1)
+    y = out["v_rot"]
+    assert np.all(np.abs(yhat - y) <= np.repeat(s, g, axis=-1) / 2 * (1 + 1e-9))
+    grp = np.abs(codes.reshape(T, hk, d // g, g)).max(-1)
+    assert np.all(grp == 7)                               # every group's absmax maps to +-7
+    assert np.array_equal(out["v_scale32"], (np.abs(y.reshape(T, hk, d // g, g)).max(-1) / 7).astype(np.float32))
+
+
+def test_v_rotation_folds_into_the_output_projection(orc):
+    """A . V~ . H^T / sqrt(d) = A . V for attention weights A: the transform on V is
+    undone by the Hadamard that the output projection absorbs."""
+    from scipy.linalg import hadamard
+    rng = _rng(50)
+    T, hk, d = 24, 1, 64
+    v = rng.standard_normal((T, hk, d)).astype(np.float32)
+    out = orc.quantize_v(orc.shape(1, hk, d, 5e5), v, d)
+    logits = rng.standard_normal((7, T))
+    A = np.exp(logits) / np.exp(logits).sum(1, keepdims=True)
+    H = hadamard(d).astype(np.float64) / math.sqrt(d)
+    back = (A @ out["v_rot"][:, 0, :]) @ H
+    assert np.max(np.abs(back - A @ v[:, 0, :].astype(np.float64))) < 1e-12
+
+
+def test_v_one_hot_row_spreads_evenly(orc):
+    d = 128
+    v = np.zeros((1, 1, d), np.float32)
+    v[0, 0, 37] = 8.0
+    out = orc.quantize_v(orc.shape(1, 1, d, 5e5), v, 32)
+    assert np.allclose(np.abs(out["v_rot"]), 8.0 / math.sqrt(d), rtol=0, atol=1e-15)
+    assert np.all(np.abs(_unpack(out["v_codes"])) == 7)
+
+
+def test_v_equals_k_path_at_position_zero_without_pair_angles(orc):
+    """At p = 0 with no pair rotation and b = d the K transform reduces to H_d / sqrt(d):
+    the V and K caches must then hold the same codes and scales."""
+    rng = _rng(51)
+    T, hk, d, g = 6, 2, 64, 16
+    x = (rng.standard_normal((T, hk, d)) * 3).astype(np.float32)
+    shp = orc.shape(0, hk, d, 5e5)
+    kv = orc.rotate_quantize_qk(shp, None, x, np.zeros(T, np.int32), None, d, g)
+    vv = orc.quantize_v(shp, x, g)
+    assert np.array_equal(kv["k_codes"], vv["v_codes"]) and np.array_equal(kv["k_scales"], vv["v_scales"])
+    assert np.max(np.abs(kv["k_rot"] - vv["v_rot"])) < 1e-13
+
+
+def test_v_slot_mapping_and_padding(orc):
+    rng = _rng(52)
+    T, hk, d, g = 4, 2, 64, 64
+    v = rng.standard_normal((T, hk, d)).astype(np.float32)
+    slots = np.array([5, -1, 0, 9], np.int64)
+    out = orc.quantize_v(orc.shape(2, hk, d, 5e5), v, g, slot_mapping=slots, n_slots=8)
+    ident = orc.quantize_v(orc.shape(2, hk, d, 5e5), v, g)
+    assert np.array_equal(out["v_codes"][5], ident["v_codes"][0])
+    assert np.array_equal(out["v_codes"][0], ident["v_codes"][2])
+    written = {0, 5}
+    for sl in range(8):
+        if sl not in written:
+            assert not out["v_codes"][sl].any() and not out["v_scales"][sl].any()

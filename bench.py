@@ -110,6 +110,32 @@ def decode_latency_us(dev, stream, reps=50):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b, g, reps=50):
+    """The same prefill launch with the V half of the KV4 cache written too
+    (one more read stream: V rows through the full-head Hadamard into INT4)."""
+    import torch
+    import rotation_rope_pair_amd as rrp
+    from rotation_rope_pair_amd import workloads as W
+    v = to_device_bf16(W.make_v(w.number), dev)
+    vc, vs = rrp.new_kv4_cache(w.n_tokens, w.n_kv_heads, w.head_dim, g, dev)
+
+    def launch():
+        rrp.rotate_quantize_qkv(shape, q, k, v, pos, support_b=b, group=g, k_codes=codes, k_scales=scales,
+                                v_codes=vc, v_scales=vs, angles=angles, q_out=q_out)
+    for _ in range(10):
+        launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = w.bytes_per_token(group=g, with_slot=False, with_v=True) * w.n_tokens
+    return {"rotate_quantize_qkv_ms": ms, "qkv_bytes_per_launch": nbytes,
+            "qkv_hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "qkv_tokens_per_s": w.n_tokens / (ms * 1e-3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,21 +175,30 @@ def main():
     rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
     supporting = {}
     if not args.hot_path_only:
-        moments.zero_()
+        reps = 10
         torch.cuda.synchronize()
         ev[0].record(stream)
-        rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
+        for _ in range(reps):
+            moments.zero_()
+            rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
         ev[1].record(stream)
         # Supporting pass 2: the K-range / quantisation-error diagnostic at b = 128.
         stats = torch.empty(8, dtype=torch.float64, device=dev)
         rrp.quant_error_stats(shape, k, pos, support_b=b, group=g, stats_out=stats, angles=angles)
         ev[2].record(stream)
-        rrp.quant_error_stats(shape, k, pos, support_b=b, group=g, stats_out=stats, angles=angles)
+        for _ in range(reps):
+            rrp.quant_error_stats(shape, k, pos, support_b=b, group=g, stats_out=stats, angles=angles)
         ev[3].record(stream)
         torch.cuda.synchronize()
         st = stats.cpu().numpy()
-        supporting.update({"calibrate_angles_ms": ev[0].elapsed_time(ev[1]),
-                           "quant_error_stats_ms": ev[2].elapsed_time(ev[3]),
+        calib_bytes = (hq + hk) * d * 2 * T + 4 * T
+        stats_bytes = hk * d * 2 * T + 4 * T
+        cal_ms = ev[0].elapsed_time(ev[1]) / reps
+        st_ms = ev[2].elapsed_time(ev[3]) / reps
+        supporting.update({"calibrate_angles_ms": cal_ms,
+                           "calibrate_angles_hbm_gbs": calib_bytes / (cal_ms * 1e-3) / 1e9,
+                           "quant_error_stats_ms": st_ms,
+                           "quant_error_stats_hbm_gbs": stats_bytes / (st_ms * 1e-3) / 1e9,
                            "rel_quant_error_b128": float(np.sqrt(st[0] / st[1])),
                            "mean_k_range_b128": float(st[2] / st[5])})
     torch.cuda.synchronize()
@@ -201,6 +236,7 @@ def main():
                 "ms": copy_ms, "GBs": copy_bytes / (copy_ms * 1e-3) / 1e9}
     if not args.hot_path_only:
         supporting["decode256_rotate_quantize_us"] = decode_latency_us(dev, stream)
+        supporting.update(qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b, g))
 
     out = {
         "metric": METRIC,

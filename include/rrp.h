@@ -119,6 +119,32 @@ int rrp_rotate_quantize_qk(const rrp_shape* shape, int32_t dtype, const void* q,
                            uint16_t* k_scales, const int64_t* slot_mapping, int64_t n_slots,
                            float* q_rot_f32, float* k_rot_f32, float* k_scale_f32, void* stream);
 
+/* rrp_rotate_quantize_qkv -- rrp_rotate_quantize_qk plus the V half of the KV4
+ * cache in the same launch (LLM rotation-quantisation notes, section 3.2.2: V
+ * is multiplied online by the head-wise Hadamard so the value cache loses its
+ * outliers; the Hadamard left on the attention output folds into the output
+ * projection offline).
+ *
+ * Q and K rows exactly as rrp_rotate_quantize_qk.  V rows get no RoPE and no
+ * pair rotation, and always the full-head transform:
+ *   y = H_d / sqrt(head_dim) . v
+ * then the K quantiser with the same `group` (same scale rule, codes and
+ * nibble order), written at the same slot.
+ *
+ * v             [n_tokens][n_kv_heads][head_dim] in `dtype`, 16-byte aligned, required.
+ * v_codes       uint8 [n_slots][n_kv_heads][head_dim/2] (alignment as k_codes), required.
+ * v_scales      uint16 (fp16 bits) [n_slots][n_kv_heads][head_dim/group], required.
+ * v_rot_f32     optional fp32 copy of transformed V, [n_tokens][n_kv_heads][head_dim], 16-B aligned.
+ * v_scale_f32   optional fp32 V group scales indexed by token, like k_scale_f32.
+ * Every other argument, and the error behaviour, as rrp_rotate_quantize_qk. */
+int rrp_rotate_quantize_qkv(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
+                            const void* v, const int32_t* pos, int64_t n_tokens, const float* angles,
+                            int32_t support_b, int32_t group, void* q_out, uint8_t* k_codes,
+                            uint16_t* k_scales, uint8_t* v_codes, uint16_t* v_scales,
+                            const int64_t* slot_mapping, int64_t n_slots, float* q_rot_f32,
+                            float* k_rot_f32, float* k_scale_f32, float* v_rot_f32, float* v_scale_f32,
+                            void* stream);
+
 /* rrp_calibrate_angles -- the calibration pass ("optimisation objective" and
  * "estimator strategies" sections: a closed-form shared angle per pair that
  * minimises the larger of the pair's two channel variances under a

@@ -16,8 +16,8 @@ RRP_EST_DEFAULT, RRP_EST_K_ONLY, RRP_EST_STREAM_BALANCED = 0, 1, 2
 RRP_ROPE_HALF_SPLIT, RRP_ROPE_INTERLEAVED = 0, 1
 
 # Symbols declared in include/rrp.h.
-EXPORTS = ("rrp_rotate_quantize_qk", "rrp_calibrate_angles", "rrp_quant_error_stats",
-           "rrp_status_string", "rrp_version")
+EXPORTS = ("rrp_rotate_quantize_qk", "rrp_rotate_quantize_qkv", "rrp_calibrate_angles",
+           "rrp_quant_error_stats", "rrp_status_string", "rrp_version")
 
 
 class RrpShape(ctypes.Structure):
@@ -51,9 +51,11 @@ def load():
     sp = ctypes.POINTER(RrpShape)
     L.rrp_rotate_quantize_qk.argtypes = [sp, i32, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, i64,
                                          vp, vp, vp, vp]
+    L.rrp_rotate_quantize_qkv.argtypes = [sp, i32, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, vp, vp,
+                                          i64, vp, vp, vp, vp, vp, vp]
     L.rrp_calibrate_angles.argtypes = [sp, i32, vp, vp, vp, i64, i32, vp, vp, vp]
     L.rrp_quant_error_stats.argtypes = [sp, i32, vp, vp, i64, vp, i32, i32, vp, vp]
-    for f in ("rrp_rotate_quantize_qk", "rrp_calibrate_angles", "rrp_quant_error_stats"):
+    for f in ("rrp_rotate_quantize_qk", "rrp_rotate_quantize_qkv", "rrp_calibrate_angles", "rrp_quant_error_stats"):
         getattr(L, f).restype = ctypes.c_int
     L.rrp_status_string.argtypes = [ctypes.c_int]
     L.rrp_status_string.restype = ctypes.c_char_p

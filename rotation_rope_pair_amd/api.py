@@ -53,8 +53,8 @@ def _stream_ptr(stream, device) -> ctypes.c_void_p:
 
 
 def new_kv4_cache(n_slots: int, n_kv_heads: int, head_dim: int, group: int, device="cuda"):
-    """Allocate an empty KV4 K cache: packed codes uint8 [n_slots][Hkv][d/2] and
-    fp16 scales [n_slots][Hkv][d/group]."""
+    """Allocate one empty half (K or V) of a KV4 cache: packed codes uint8
+    [n_slots][Hkv][d/2] and fp16 scales [n_slots][Hkv][d/group]."""
     codes = torch.zeros((n_slots, n_kv_heads, head_dim // 2), dtype=torch.uint8, device=device)
     scales = torch.zeros((n_slots, n_kv_heads, head_dim // group), dtype=torch.float16, device=device)
     return codes, scales
@@ -65,6 +65,40 @@ def new_moments(head_dim: int, device="cuda") -> torch.Tensor:
     return torch.zeros((head_dim // 2, 2, 6), dtype=torch.float64, device=device)
 
 
+def _rotate_args(shape, q, k, v, pos, support_b, group, k_codes, k_scales, v_codes, v_scales, angles, q_out,
+                 slot_mapping, n_slots, q_rot_f32, k_rot_f32, k_scale_f32, v_rot_f32, v_scale_f32, stream):
+    d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    T = int(pos.numel())
+    dt = k.dtype
+    dev = k.device
+    if n_slots is None:
+        n_slots = int(k_codes.shape[0])
+    ng = max(1, d // max(1, int(group)))
+    for name, c in (("k_codes", k_codes), ("v_codes", v_codes)):
+        if c is not None and n_slots * hk * (d // 2) > c.numel():
+            raise ValueError(f"{name} is smaller than n_slots * n_kv_heads * head_dim / 2")
+    head = [ctypes.byref(shape), _dtype_code(k),
+            _dev(q, "q", T * hq * d, dt, dev), _dev(k, "k", T * hk * d, dt, dev)]
+    if v is not None:
+        head.append(_dev(v, "v", T * hk * d, dt, dev))
+    mid = [_dev(pos, "pos", T, torch.int32, dev), T,
+           _dev(angles, "angles", d // 2, torch.float32, dev), int(support_b), int(group),
+           _dev(q_out, "q_out", T * hq * d, dt, dev),
+           _dev(k_codes, "k_codes", n_slots * hk * (d // 2), torch.uint8, dev),
+           _dev(k_scales, "k_scales", n_slots * hk * ng, (torch.float16, torch.int16), dev)]
+    if v is not None:
+        mid += [_dev(v_codes, "v_codes", n_slots * hk * (d // 2), torch.uint8, dev),
+                _dev(v_scales, "v_scales", n_slots * hk * ng, (torch.float16, torch.int16), dev)]
+    tail = [_dev(slot_mapping, "slot_mapping", T, torch.int64, dev), int(n_slots),
+            _dev(q_rot_f32, "q_rot_f32", T * hq * d, torch.float32, dev),
+            _dev(k_rot_f32, "k_rot_f32", T * hk * d, torch.float32, dev),
+            _dev(k_scale_f32, "k_scale_f32", T * hk * ng, torch.float32, dev)]
+    if v is not None:
+        tail += [_dev(v_rot_f32, "v_rot_f32", T * hk * d, torch.float32, dev),
+                 _dev(v_scale_f32, "v_scale_f32", T * hk * ng, torch.float32, dev)]
+    return head + mid + tail + [_stream_ptr(stream, dev)]
+
+
 def rotate_quantize_qk(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor, pos: torch.Tensor, *,
                        support_b: int, group: int, k_codes: torch.Tensor, k_scales: torch.Tensor,
                        angles: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None,
@@ -73,30 +107,29 @@ def rotate_quantize_qk(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tens
                        k_scale_f32: Optional[torch.Tensor] = None, stream=None) -> None:
     """Enqueue rrp_rotate_quantize_qk (see include/rrp.h)."""
     L = _abi.load()
-    d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
-    T = int(pos.numel())
-    dt = k.dtype
-    dev = k.device
-    if n_slots is None:
-        n_slots = int(k_codes.shape[0])
-    if n_slots * hk * (d // 2) > k_codes.numel():
-        raise ValueError("k_codes is smaller than n_slots * n_kv_heads * head_dim / 2")
-    args = [
-        ctypes.byref(shape), _dtype_code(k),
-        _dev(q, "q", T * hq * d, dt, dev), _dev(k, "k", T * hk * d, dt, dev),
-        _dev(pos, "pos", T, torch.int32, dev), T,
-        _dev(angles, "angles", d // 2, torch.float32, dev), int(support_b), int(group),
-        _dev(q_out, "q_out", T * hq * d, dt, dev),
-        _dev(k_codes, "k_codes", n_slots * hk * (d // 2), torch.uint8, dev),
-        _dev(k_scales, "k_scales", n_slots * hk * max(1, d // max(1, int(group))),
-             (torch.float16, torch.int16), dev),
-        _dev(slot_mapping, "slot_mapping", T, torch.int64, dev), int(n_slots),
-        _dev(q_rot_f32, "q_rot_f32", T * hq * d, torch.float32, dev),
-        _dev(k_rot_f32, "k_rot_f32", T * hk * d, torch.float32, dev),
-        _dev(k_scale_f32, "k_scale_f32", T * hk * max(1, d // max(1, int(group))), torch.float32, dev),
-        _stream_ptr(stream, dev),
-    ]
+    args = _rotate_args(shape, q, k, None, pos, support_b, group, k_codes, k_scales, None, None, angles, q_out,
+                        slot_mapping, n_slots, q_rot_f32, k_rot_f32, k_scale_f32, None, None, stream)
     _abi.check("rrp_rotate_quantize_qk", L.rrp_rotate_quantize_qk(*args))
+
+
+def rotate_quantize_qkv(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor,
+                        pos: torch.Tensor, *, support_b: int, group: int, k_codes: torch.Tensor,
+                        k_scales: torch.Tensor, v_codes: torch.Tensor, v_scales: torch.Tensor,
+                        angles: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None,
+                        slot_mapping: Optional[torch.Tensor] = None, n_slots: Optional[int] = None,
+                        q_rot_f32: Optional[torch.Tensor] = None, k_rot_f32: Optional[torch.Tensor] = None,
+                        k_scale_f32: Optional[torch.Tensor] = None, v_rot_f32: Optional[torch.Tensor] = None,
+                        v_scale_f32: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue rrp_rotate_quantize_qkv: the Q/K path plus the V half of the KV4
+    cache in one launch (see include/rrp.h)."""
+    L = _abi.load()
+    if v is None or v_codes is None or v_scales is None:
+        raise ValueError("rotate_quantize_qkv needs v, v_codes and v_scales")
+    if v.dtype != k.dtype:
+        raise TypeError("v must have the dtype of k")
+    args = _rotate_args(shape, q, k, v, pos, support_b, group, k_codes, k_scales, v_codes, v_scales, angles, q_out,
+                        slot_mapping, n_slots, q_rot_f32, k_rot_f32, k_scale_f32, v_rot_f32, v_scale_f32, stream)
+    _abi.check("rrp_rotate_quantize_qkv", L.rrp_rotate_quantize_qkv(*args))
 
 
 def calibrate_angles(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor, pos: torch.Tensor, *,
@@ -136,6 +169,6 @@ def quant_error_stats(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, su
     _abi.check("rrp_quant_error_stats", L.rrp_quant_error_stats(*args))
 
 
-__all__ = ["layer_shape", "rotate_quantize_qk", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
+__all__ = ["layer_shape", "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
            "new_moments", "RrpError", "RrpShape", "ESTIMATORS", "RRP_F32", "RRP_BF16",
            "RRP_ROPE_HALF_SPLIT", "RRP_ROPE_INTERLEAVED"]

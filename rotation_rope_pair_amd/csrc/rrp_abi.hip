@@ -72,11 +72,14 @@ RRP_EXPORT const char* rrp_status_string(int status) {
     }
 }
 
-RRP_EXPORT int rrp_rotate_quantize_qk(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
-                                      const int32_t* pos, int64_t n_tokens, const float* angles,
-                                      int32_t support_b, int32_t group, void* q_out, uint8_t* k_codes,
-                                      uint16_t* k_scales, const int64_t* slot_mapping, int64_t n_slots,
-                                      float* q_rot_f32, float* k_rot_f32, float* k_scale_f32, void* stream) {
+namespace {
+
+// Shared body of the Q/K and Q/K/V entry points (v == nullptr: no V rows).
+int rotate_quantize(const rrp_shape* shape, int32_t dtype, const void* q, const void* k, const void* v,
+                    const int32_t* pos, int64_t n_tokens, const float* angles, int32_t support_b, int32_t group,
+                    void* q_out, uint8_t* k_codes, uint16_t* k_scales, uint8_t* v_codes, uint16_t* v_scales,
+                    const int64_t* slot_mapping, int64_t n_slots, float* q_rot_f32, float* k_rot_f32,
+                    float* k_scale_f32, float* v_rot_f32, float* v_scale_f32, void* stream) {
     int st = check_shape(shape, dtype);
     if (st != RRP_OK) return st;
     if ((st = check_b_g(shape, support_b, group)) != RRP_OK) return st;
@@ -84,9 +87,12 @@ RRP_EXPORT int rrp_rotate_quantize_qk(const rrp_shape* shape, int32_t dtype, con
     if (k == nullptr || pos == nullptr || k_codes == nullptr || k_scales == nullptr) return RRP_ERR_INVALID_ARG;
     if ((q_out != nullptr || q_rot_f32 != nullptr) && q == nullptr) return RRP_ERR_INVALID_ARG;
     if (slot_mapping == nullptr && n_slots < n_tokens) return RRP_ERR_INVALID_ARG;
+    const uintptr_t code_align = dtype == RRP_F32 ? 2 : 4;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_out, 16) || !aligned(q_rot_f32, 16) ||
         !aligned(k_rot_f32, 16) || !aligned(k_scale_f32, 4) || !aligned(pos, 4) || !aligned(angles, 4) ||
-        !aligned(k_codes, dtype == RRP_F32 ? 2 : 4) || !aligned(k_scales, 2) || !aligned(slot_mapping, 8))
+        !aligned(k_codes, code_align) || !aligned(k_scales, 2) || !aligned(slot_mapping, 8) ||
+        !aligned(v, 16) || !aligned(v_codes, code_align) || !aligned(v_scales, 2) || !aligned(v_rot_f32, 16) ||
+        !aligned(v_scale_f32, 4))
         return RRP_ERR_MISALIGNED;
     if (n_tokens == 0) return RRP_OK;
 
@@ -102,6 +108,11 @@ RRP_EXPORT int rrp_rotate_quantize_qk(const rrp_shape* shape, int32_t dtype, con
     a.q_dbg = q_rot_f32;
     a.k_dbg = k_rot_f32;
     a.s_dbg = k_scale_f32;
+    a.v = v;
+    a.v_codes = v_codes;
+    a.v_scales = v_scales;
+    a.v_dbg = v_rot_f32;
+    a.vs_dbg = v_scale_f32;
     a.n_tokens = n_tokens;
     a.n_slots = n_slots;
     a.hq = shape->n_q_heads;
@@ -110,9 +121,35 @@ RRP_EXPORT int rrp_rotate_quantize_qk(const rrp_shape* shape, int32_t dtype, con
     a.support_b = support_b;
     a.group = group;
     a.rsqrt_b = 1.0 / sqrt((double)support_b);
+    a.rsqrt_v = 1.0 / sqrt((double)shape->head_dim);
     fill_inv_freq(shape, a.inv_freq);
     hipError_t e = rrp::launch_rotate_quantize(a, dtype, shape->head_dim, shape->rope_layout, (hipStream_t)stream);
     return e == hipSuccess ? RRP_OK : RRP_ERR_HIP;
+}
+
+}  // namespace
+
+RRP_EXPORT int rrp_rotate_quantize_qk(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
+                                      const int32_t* pos, int64_t n_tokens, const float* angles,
+                                      int32_t support_b, int32_t group, void* q_out, uint8_t* k_codes,
+                                      uint16_t* k_scales, const int64_t* slot_mapping, int64_t n_slots,
+                                      float* q_rot_f32, float* k_rot_f32, float* k_scale_f32, void* stream) {
+    return rotate_quantize(shape, dtype, q, k, nullptr, pos, n_tokens, angles, support_b, group, q_out, k_codes,
+                           k_scales, nullptr, nullptr, slot_mapping, n_slots, q_rot_f32, k_rot_f32, k_scale_f32,
+                           nullptr, nullptr, stream);
+}
+
+RRP_EXPORT int rrp_rotate_quantize_qkv(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
+                                       const void* v, const int32_t* pos, int64_t n_tokens, const float* angles,
+                                       int32_t support_b, int32_t group, void* q_out, uint8_t* k_codes,
+                                       uint16_t* k_scales, uint8_t* v_codes, uint16_t* v_scales,
+                                       const int64_t* slot_mapping, int64_t n_slots, float* q_rot_f32,
+                                       float* k_rot_f32, float* k_scale_f32, float* v_rot_f32, float* v_scale_f32,
+                                       void* stream) {
+    if (v == nullptr || v_codes == nullptr || v_scales == nullptr) return RRP_ERR_INVALID_ARG;
+    return rotate_quantize(shape, dtype, q, k, v, pos, n_tokens, angles, support_b, group, q_out, k_codes,
+                           k_scales, v_codes, v_scales, slot_mapping, n_slots, q_rot_f32, k_rot_f32, k_scale_f32,
+                           v_rot_f32, v_scale_f32, stream);
 }
 
 RRP_EXPORT int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,

@@ -24,6 +24,11 @@ struct RotateArgs {
     float* q_dbg;
     float* k_dbg;
     float* s_dbg;
+    const void* v;       // NULL: no V rows
+    uint8_t* v_codes;
+    uint16_t* v_scales;
+    float* v_dbg;
+    float* vs_dbg;
     int64_t n_tokens;
     int64_t n_slots;
     int32_t hq;       // Q heads in the tensor layout
@@ -32,6 +37,7 @@ struct RotateArgs {
     int32_t support_b;
     int32_t group;
     double rsqrt_b;
+    double rsqrt_v;  // 1 / sqrt(head_dim)
     float inv_freq[kMaxPairs];
 };
 

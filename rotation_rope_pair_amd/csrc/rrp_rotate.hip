@@ -106,7 +106,9 @@ template <int R> struct Depth {
 };
 
 // BT: compile-time Hadamard support (BT == D, the full-head case) or 0 (runtime b).
-template <typename E, int D, int LAYOUT, bool SMALLG, int BT>
+// HAS_V: also turn the V rows by the full-head Hadamard and quantise them into
+// the V half of the cache (no RoPE, no pair rotation).
+template <typename E, int D, int LAYOUT, bool SMALLG, int BT, bool HAS_V>
 __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a) {
     using G = Geo<E, D>;
     using LM = LaneMap<G::L>;
@@ -131,6 +133,7 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
     const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
     // Rows are loaded permuted (lane s holds position s ^ perm), see fwht_row.
     const int s_src = s ^ lane_perm_mask<D, CE>(BT ? BT : a.support_b);
+    const int s_src_v = s ^ lane_perm_mask<D, CE>(D);  // V: full-head support
     int kidx[CE];
     pair_index_of_lane<D, LAYOUT, CE>(s_src, kidx);
 
@@ -139,6 +142,7 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
     const int ngroups = D / a.group;
     const unsigned char* qb = static_cast<const unsigned char*>(a.q);
     const unsigned char* kb = static_cast<const unsigned char*>(a.k);
+    const unsigned char* vb = static_cast<const unsigned char*>(a.v);
     unsigned char* qo = static_cast<unsigned char*>(a.q_out);
     const int ld_off = grp * ROWB;  // this lane's row inside a pass
 
@@ -149,16 +153,22 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
         // wave-uniform row bases of this token
         const unsigned char* qt = qb + (size_t)t * a.hq * ROWB;
         const unsigned char* kt = kb + (size_t)t * hk * ROWB;
+        const unsigned char* vt = vb + (size_t)t * hk * ROWB;
         unsigned char* qot = qo + (size_t)t * a.hq * ROWB;
 
-        // Issue the loads of the first MQ Q passes and MK K passes.
-        u32x4 rq[MQ][2], rk[MK][2];
+        // Issue the loads of the first MQ Q passes and MK K passes (and V passes).
+        u32x4 rq[MQ][2], rk[MK][2], rv[HAS_V ? MK : 1][2];
 #pragma unroll
         for (int i = 0; i < MQ; ++i)
             if (i < nq && i * R + grp < hq) load_row_chunks<E, D>(qt + i * R * ROWB + ld_off, s_src, rq[i]);
 #pragma unroll
         for (int i = 0; i < MK; ++i)
             if (i < nk && i * R + grp < hk) load_row_chunks<E, D>(kt + i * R * ROWB + ld_off, s_src, rk[i]);
+        if constexpr (HAS_V) {
+#pragma unroll
+            for (int i = 0; i < MK; ++i)
+                if (i < nk && i * R + grp < hk) load_row_chunks<E, D>(vt + i * R * ROWB + ld_off, s_src_v, rv[i]);
+        }
 
         token_tables<D, FOLD>(tab32, tab64, lane, p, invf, cphi, sphi, a.rsqrt_b);
 
@@ -237,6 +247,50 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
                                                     a.s_dbg ? a.s_dbg + trow * ngroups : nullptr, in_cache);
             }
         }
+
+        // ---- V rows (KV precision): H_D / sqrt(D), then the K quantiser ----
+        if constexpr (HAS_V) {
+            for (int c0 = 0; c0 < nk; c0 += MK) {
+                if (c0 > 0) {
+#pragma unroll
+                    for (int i = 0; i < MK; ++i)
+                        if (c0 + i < nk && (c0 + i) * R + grp < hk)
+                            load_row_chunks<E, D>(vt + (c0 + i) * R * ROWB + ld_off, s_src_v, rv[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < MK; ++i) {
+                    const int pass = c0 + i;
+                    if (pass >= nk) break;
+                    const int h = pass * R + grp;
+                    if (h >= hk) continue;
+                    float xf[2][CE];
+                    unpack_chunk<E, CE>(rv[i][0], xf[0]);
+                    unpack_chunk<E, CE>(rv[i][1], xf[1]);
+                    KV x[2][CE];
+#pragma unroll
+                    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                        for (int i2 = 0; i2 < CE; ++i2) x[ch][i2] = (KV)xf[ch][i2];
+                    fwht_row<D, CE, D, false>(x, D, s);
+#pragma unroll
+                    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                        for (int i2 = 0; i2 < CE; ++i2) x[ch][i2] *= (KV)a.rsqrt_v;
+                    const size_t trow = (size_t)t * hk + h;
+                    if (a.v_dbg) {
+                        float* dst = a.v_dbg + trow * D;
+#pragma unroll
+                        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                            for (int i2 = 0; i2 < CE; ++i2) dst[ch * P + s * CE + i2] = (float)x[ch][i2];
+                    }
+                    const size_t crow = in_cache ? (size_t)slot * hk + h : 0;
+                    quantize_store_k_row<D, CE, SMALLG>(x, s, a.group, a.v_codes + crow * (D / 2),
+                                                        a.v_scales + crow * ngroups,
+                                                        a.vs_dbg ? a.vs_dbg + trow * ngroups : nullptr, in_cache);
+                }
+            }
+        }
     }
 }
 
@@ -251,13 +305,18 @@ hipError_t launch_t(const RotateArgs& a, hipStream_t st) {
     if (blocks > RRP_MAX_BLOCKS) blocks = RRP_MAX_BLOCKS;  // waves then walk several tokens each
     const bool smallg = a.group < Geo<E, D>::CE;
     const dim3 grid((unsigned)blocks), block(64 * wpb);
-    if (a.support_b == D) {
-        if (smallg) hipLaunchKernelGGL((rotate_quantize_kernel<E, D, LAYOUT, true, D>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((rotate_quantize_kernel<E, D, LAYOUT, false, D>), grid, block, 0, st, a);
+#define RRP_LAUNCH(SG, BT, HV) \
+    hipLaunchKernelGGL((rotate_quantize_kernel<E, D, LAYOUT, SG, BT, HV>), grid, block, 0, st, a)
+#define RRP_LAUNCH_B(SG, HV)           \
+    if (a.support_b == D) RRP_LAUNCH(SG, D, HV); \
+    else RRP_LAUNCH(SG, 0, HV)
+    if (a.v != nullptr) {
+        if (smallg) { RRP_LAUNCH_B(true, true); } else { RRP_LAUNCH_B(false, true); }
     } else {
-        if (smallg) hipLaunchKernelGGL((rotate_quantize_kernel<E, D, LAYOUT, true, 0>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((rotate_quantize_kernel<E, D, LAYOUT, false, 0>), grid, block, 0, st, a);
+        if (smallg) { RRP_LAUNCH_B(true, false); } else { RRP_LAUNCH_B(false, false); }
     }
+#undef RRP_LAUNCH_B
+#undef RRP_LAUNCH
     return hipGetLastError();
 }
 

@@ -148,6 +148,14 @@ def positions(w: Workload, n_tokens: int, rng=None) -> np.ndarray:
     return (np.arange(n_tokens, dtype=np.int64) % L).astype(np.int32)
 
 
+def make_v(number: int, n_tokens: Optional[int] = None) -> np.ndarray:
+    """V rows [T][Hkv][d] of workload `number` (K's recipe, streams 6 and 7)."""
+    w = WORKLOADS[number]
+    T = w.n_tokens if n_tokens is None else int(n_tokens)
+    seed = 1000 + number
+    return _draw_samples((seed, 6), w, _draw_params(_rng(seed, 7), w, w.n_kv_heads), T)
+
+
 def make_inputs(number: int, n_tokens: Optional[int] = None, want_q: bool = True, want_v: bool = False):
     """Inputs of workload `number`: dict(q, k, v, pos, slot_mapping, n_slots, calib).
 
@@ -173,7 +181,7 @@ def make_inputs(number: int, n_tokens: Optional[int] = None, want_q: bool = True
     res["pos"] = pos
     res["q"] = _draw_samples((seed, 2), w, pq, T) if want_q else None
     res["k"] = _draw_samples((seed, 3), w, pk, T)
-    res["v"] = _draw_samples((seed, 6), w, _draw_params(_rng(seed, 7), w, w.n_kv_heads), T) if want_v else None
+    res["v"] = make_v(number, T) if want_v else None
     res["calib"] = None
     if w.calib_tokens:
         Tc = w.calib_tokens

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["rrp_calibrate_angles", "rrp_quant_error_stats", "rrp_rotate_quantize_qk",
-                                           "rrp_status_string", "rrp_version"])
+                                           "rrp_rotate_quantize_qkv", "rrp_status_string", "rrp_version"])
 
 
 def test_library_exports_exactly_the_declared_symbols(lib):
@@ -84,6 +84,16 @@ def test_rotate_validation(lib):
     assert rot(lib, k=P2) == 2 and rot(lib, q=P2, q_out=P16) == 2
     assert rot(lib, codes=P2) == 2 and rot(lib, kd=P2) == 2
     assert rot(lib, slots=ctypes.c_void_p((1 << 20) + 4)) == 2
+
+
+def test_rotate_qkv_validation(lib):
+    def rqkv(v=P16, vc=P16, vs=P16, T=4, vd=None, vsd=None, k=P16):
+        return lib.rrp_rotate_quantize_qkv(ctypes.byref(_shape()), 1, None, k, v, P16, T, None, 128, 128, None,
+                                           P16, P16, vc, vs, None, 4, None, None, None, vd, vsd, None)
+    assert rqkv(T=0) == 0
+    assert rqkv(v=None) == 1 and rqkv(vc=None) == 1 and rqkv(vs=None) == 1 and rqkv(k=None) == 1
+    assert rqkv(v=P2) == 2 and rqkv(vc=P2) == 2 and rqkv(vd=P2) == 2
+    assert rqkv(vs=ctypes.c_void_p((1 << 20) + 1)) == 2
 
 
 def test_calibrate_validation(lib):

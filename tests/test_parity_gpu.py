@@ -284,6 +284,105 @@ def test_rotate_is_deterministic():
 
 
 # ---------------------------------------------------------------------------
+# rotate + quantise with the V half of the cache
+# ---------------------------------------------------------------------------
+
+_VINPUTS = {}
+
+
+def vinputs(n, T=None):
+    key = (n, T)
+    if key not in _VINPUTS:
+        if T is None:  # reuse the full-size Q / K already drawn
+            _VINPUTS[key] = dict(inputs(n), v=W.make_v(n))
+        else:
+            _VINPUTS[key] = W.make_inputs(n, n_tokens=T, want_v=True)
+    return _VINPUTS[key]
+
+
+def run_rotate_qkv(w, inp, angles, b, g, *, debug=True):
+    d, hq, hk = w.head_dim, w.n_q_heads, w.n_kv_heads
+    q, k, v, pos = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["pos"])
+    T = int(pos.numel())
+    n_slots = inp.get("n_slots", T)
+    kc, ks = rrp.new_kv4_cache(n_slots, hk, d, g, DEV)
+    vc, vs = rrp.new_kv4_cache(n_slots, hk, d, g, DEV)
+    dbg = {}
+    if debug:
+        dbg = {"q_rot_f32": torch.empty((T, hq, d), dtype=torch.float32, device=DEV),
+               "k_rot_f32": torch.empty((T, hk, d), dtype=torch.float32, device=DEV),
+               "k_scale_f32": torch.empty((T, hk, d // g), dtype=torch.float32, device=DEV),
+               "v_rot_f32": torch.empty((T, hk, d), dtype=torch.float32, device=DEV),
+               "v_scale_f32": torch.empty((T, hk, d // g), dtype=torch.float32, device=DEV)}
+    q_out = torch.empty_like(q)
+    rrp.rotate_quantize_qkv(shape_of(w), q, k, v, pos, support_b=b, group=g, k_codes=kc, k_scales=ks,
+                            v_codes=vc, v_scales=vs, angles=None if angles is None else to_dev(angles), q_out=q_out,
+                            slot_mapping=to_dev(inp.get("slot_mapping")), n_slots=n_slots, **dbg)
+    torch.cuda.synchronize()
+    return {"q_out": q_out, "codes": kc, "scales": ks, "v_codes": vc, "v_scales": vs, **dbg}
+
+
+def check_v(w, inp, out, g, idx):
+    d, hk = w.head_dim, w.n_kv_heads
+    idx = np.asarray(idx)
+    ref = O.quantize_v(oshape_of(w), inp["v"][idx], g)
+    sm = inp.get("slot_mapping")
+    slots = idx if sm is None else sm[idx]
+    sl = torch.from_numpy(slots.astype(np.int64)).to(DEV)
+    it = torch.from_numpy(idx.astype(np.int64)).to(DEV)
+    codes = out["v_codes"].index_select(0, sl).cpu().numpy().reshape(-1, d // 2)
+    scales = bits(out["v_scales"].index_select(0, sl)).reshape(-1, d // g)
+    kw = {}
+    if "v_rot_f32" in out:
+        kw = dict(k_rot_gpu=out["v_rot_f32"].index_select(0, it).cpu().numpy().reshape(-1, d),
+                  s32_gpu=out["v_scale_f32"].index_select(0, it).cpu().numpy().reshape(-1, d // g),
+                  s32_ref=ref["v_scale32"].reshape(-1, d // g))
+    return C.compare_k(codes, scales, ref["v_rot"].reshape(-1, d), ref["v_scales"].reshape(-1, d // g),
+                       ref["v_codes"].reshape(-1, d // 2), g, **kw)
+
+
+@pytest.mark.parametrize("n,b,g", [(1, 2, 64), (1, 64, 4), (2, 16, 64), (2, 64, 8), (3, 128, 128), (3, 2, 2)])
+def test_rotate_qkv_parity(n, b, g):
+    """Q and K as the Q/K entry point (bit for bit), V against the oracle's V side."""
+    w = W.WORKLOADS[n]
+    T = min(w.n_tokens, 1024)
+    inp = vinputs(n, T)
+    ang = random_angles(w.n_pairs, 800 + n)
+    out = run_rotate_qkv(w, inp, ang, b, g)
+    rep_k = check_rotate(w, inp, out, ang, b, g, np.arange(T))
+    rep_v = check_v(w, inp, out, g, np.arange(T))
+    ref_qk = run_rotate(w, inp, ang, b, g)
+    for key in ("q_out", "codes", "scales", "q_rot_f32", "k_rot_f32", "k_scale_f32"):
+        a, c = out[key], ref_qk[key]
+        if a.dtype == torch.bfloat16:
+            a, c = a.view(torch.int16), c.view(torch.int16)
+        assert torch.equal(a, c), key
+    print(f"workload {n} b={b} g={g}: K {rep_k} V {rep_v}")
+
+
+def test_rotate_qkv_decode_slot_scatter():
+    w = W.WORKLOADS[5]
+    inp = vinputs(5)
+    ang = random_angles(w.n_pairs, 805)
+    out = run_rotate_qkv(w, inp, ang, 128, w.group)
+    print(check_v(w, inp, out, w.group, np.arange(w.n_tokens)))
+    sl = torch.from_numpy(inp["slot_mapping"]).to(DEV)
+    assert int(torch.count_nonzero(out["v_scales"]).item()) == \
+        int(torch.count_nonzero(out["v_scales"].index_select(0, sl)).item())
+
+
+def test_rotate_qkv_prefill_128k_sampled():
+    """The 131072-token prefill with V, in the launch the benchmark times, checked
+    on 2048 sampled tokens (V against the oracle, K and Q too)."""
+    w = W.WORKLOADS[4]
+    inp = vinputs(4)
+    ang = random_angles(w.n_pairs, 804)
+    out = run_rotate_qkv(w, inp, ang, 128, 128, debug=False)
+    idx = sample_tokens(w.n_tokens, 2048, 14)
+    print(check_rotate(w, inp, out, ang, 128, 128, idx), check_v(w, inp, out, 128, idx))
+
+
+# ---------------------------------------------------------------------------
 # calibration
 # ---------------------------------------------------------------------------
 

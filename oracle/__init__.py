@@ -64,6 +64,9 @@ def lib():
         L.orc_quantize_v.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, vp, i64, ctypes.c_int, vp, vp, vp, i64,
                                      vp, vp]
         L.orc_quantize_v.restype = ctypes.c_int
+        L.orc_decode_scores.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, vp, i64, vp, vp, ctypes.c_int, i64,
+                                        vp, vp, ctypes.c_int, vp]
+        L.orc_decode_scores.restype = ctypes.c_int
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = ctypes.c_int
         for name in ("orc_rotate_quantize_qk", "orc_calibrate_moments",
@@ -225,6 +228,23 @@ def quantize_v(shp, v, group, slot_mapping=None, n_slots=None):
                               _p(out["v_scales"]), _p(sm), int(n_slots), _p(out["v_rot"]), _p(out["v_scale32"]))
     if rc != 0:
         raise ValueError("oracle quantize_v rejected its arguments")
+    return out
+
+
+def decode_scores(shp, q, k_codes, k_scales, group, seq_start, seq_len, max_len, n_slots=None):
+    """Decode logits fp64 [B][Hq][max_len] from the KV4 cache (entries past each
+    sequence's length stay -inf here, NaN for slots outside the cache)."""
+    qa, dt = _in(q)
+    B = qa.shape[0]
+    codes = _c(k_codes, np.uint8)
+    scales = _c(k_scales, np.uint16)
+    if n_slots is None:
+        n_slots = codes.shape[0]
+    out = np.full((B, shp.n_q_heads, int(max_len)), -np.inf, np.float64)
+    rc = lib().orc_decode_scores(ctypes.byref(shp), dt, _p(qa), B, _p(codes), _p(scales), int(group), int(n_slots),
+                                 _p(_c(seq_start, np.int64)), _p(_c(seq_len, np.int32)), int(max_len), _p(out))
+    if rc != 0:
+        raise ValueError("oracle decode_scores rejected its arguments")
     return out
 
 

@@ -499,6 +499,59 @@ int orc_quant_error_stats(const orc_shape* s, int dtype, const void* k, const in
     return 0;
 }
 
+/* Value of the two's-complement INT4 code held in nibble `which` (0 = low) of a byte. */
+static int nibble_code(uint8_t byte, int which)
+{
+    const int n = which ? (byte >> 4) & 0xF : byte & 0xF;
+    return n >= 8 ? n - 16 : n;
+}
+
+/* Decode attention logits read from the KV4 cache ([NOTES] section 3.2.1: the
+ * head-wise rotation cancels inside Q K^T, so the rotated query against the
+ * rotated, quantised key gives the attention logit; [QIFT] introduction: decode
+ * reads the KV cache and is memory-bound).  For sequence b, query head h (key
+ * head h * Hkv / Hq) and key j < seq_len[b] at slot seq_start[b] + j:
+ *   score = sum_c q[b][h][c] * code(slot, kv, c) * s_h(slot, kv, c / g)
+ * in fp64.  Keys whose slot lies outside [0, n_slots) give NaN; entries at
+ * j >= seq_len[b] (or j >= max_len) are not written. */
+int orc_decode_scores(const orc_shape* s, int dtype, const void* q, int64_t n_seqs,
+                      const uint8_t* k_codes, const uint16_t* k_scales, int group, int64_t n_slots,
+                      const int64_t* seq_start, const int32_t* seq_len, int max_len, double* scores)
+{
+    if (check_shape(s) || n_seqs < 0 || max_len < 0 || !q || !k_codes || !k_scales || !seq_start || !seq_len ||
+        !scores)
+        return -1;
+    const int d = s->head_dim, hq = s->n_q_heads, hk = s->n_kv_heads;
+    if (hq < 1 || hq % hk) return -1;
+    if (group < 2 || (group & 1) || d % group) return -1;
+    const int ng = d / group;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < n_seqs; ++b) {
+        double qv[ORC_MAX_DIM];
+        const int len = seq_len[b] < max_len ? seq_len[b] : max_len;
+        for (int h = 0; h < hq; ++h) {
+            const int kv = (int)((int64_t)h * hk / hq);
+            for (int c = 0; c < d; ++c) qv[c] = load_elem(q, dtype, (b * hq + h) * (int64_t)d + c);
+            double* out = scores + (b * hq + h) * (int64_t)max_len;
+            for (int j = 0; j < len; ++j) {
+                const int64_t slot = seq_start[b] + j;
+                if (slot < 0 || slot >= n_slots) {
+                    out[j] = NAN;
+                    continue;
+                }
+                const uint8_t* row = k_codes + (slot * hk + kv) * (int64_t)(d / 2);
+                const uint16_t* srow = k_scales + (slot * hk + kv) * (int64_t)ng;
+                double acc = 0.0;
+                for (int c = 0; c < d; ++c)
+                    acc += qv[c] * (double)nibble_code(row[c / 2], c & 1) * orc_f16_value(srow[c / group]);
+                out[j] = acc;
+            }
+        }
+    }
+    return 0;
+}
+
 /* Threads the token loops above may use (1 without OpenMP). */
 int orc_max_threads(void)
 {

@@ -131,6 +131,14 @@ int orc_quant_error_stats(const orc_shape* s, int dtype, const void* k, const in
                           int64_t n_tokens, const float* angles, int support_b, int group,
                           double* stats);
 
+/* Decode attention logits from the KV4 cache: scores[b][h][j] = sum_c q[b][h][c] *
+ * code * s_h for key j < min(seq_len[b], max_len) at slot seq_start[b] + j, key head
+ * h * Hkv / Hq (fp64).  q: [n_seqs][Hq][d] in `dtype`; scores: fp64 [n_seqs][Hq][max_len];
+ * NaN for slots outside [0, n_slots); entries at j >= seq_len[b] are left untouched. */
+int orc_decode_scores(const orc_shape* s, int dtype, const void* q, int64_t n_seqs,
+                      const uint8_t* k_codes, const uint16_t* k_scales, int group, int64_t n_slots,
+                      const int64_t* seq_start, const int32_t* seq_len, int max_len, double* scores);
+
 /* Threads the token-parallel entry points may use (OpenMP), 1 without OpenMP. */
 int orc_max_threads(void);
 

@@ -36,6 +36,8 @@ MUTANTS = {
     "v_half_head_hadamard": ("orc_hadamard_blocks(x, d, d, y);", "orc_hadamard_blocks(x, d, d / 2, y);"),
     "v_scale_at_token_not_slot": ("if (in_cache) v_scales[(slot * hk + h) * ng + j] = sh;",
                                   "if (in_cache) v_scales[(t * hk + h) * ng + j] = sh;"),
+    "decode_gqa_interleaved": ("const int kv = (int)((int64_t)h * hk / hq);", "const int kv = h % hk;"),
+    "decode_one_scale_per_row": ("orc_f16_value(srow[c / group])", "orc_f16_value(srow[0])"),
 }
 
 

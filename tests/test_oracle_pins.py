@@ -699,3 +699,84 @@ def test_v_slot_mapping_and_padding(orc):
     for sl in range(8):
         if sl not in written:
             assert not out["v_codes"][sl].any() and not out["v_scales"][sl].any()
+
+
+# --------------------------------------------------------------------------
+# Decode logits from the KV4 cache ([NOTES] section 3.2.1: the rotation cancels
+# inside Q K^T; [QIFT] introduction: decode reads the KV cache).
+# --------------------------------------------------------------------------
+
+def _random_cache(rng, n_slots, hk, d, g):
+    codes = rng.integers(0, 256, (n_slots, hk, d // 2), dtype=np.uint8)
+    scales = np.exp2(rng.uniform(-8, 3, (n_slots, hk, d // g))).astype(np.float16).view(np.uint16)
+    return codes, scales
+
+
+@pytest.mark.parametrize("hq,hk,d,g", [(4, 2, 64, 64), (8, 2, 128, 16), (3, 3, 64, 2), (32, 8, 128, 128)])
+def test_decode_scores_equal_numpy_dequant_matmul(orc, hq, hk, d, g):
+    rng = _rng(60 + hq + g)
+    n_slots, B, max_len = 300, 5, 70
+    codes, scales = _random_cache(rng, n_slots, hk, d, g)
+    q = rng.standard_normal((B, hq, d)).astype(np.float32)
+    start = np.array([0, 50, 120, 230, 299], np.int64)
+    lens = np.array([70, 1, 69, 70, 3], np.int32)          # the last runs past the cache: NaN
+    out = orc.decode_scores(orc.shape(hq, hk, d, 5e5), q, codes, scales, g, start, lens, max_len)
+    kdeq = _unpack(codes).astype(np.float64) * np.repeat(scales.view(np.float16).astype(np.float64), g, axis=-1)
+    for b in range(B):
+        for h in range(hq):
+            kv = h * hk // hq                               # grouped-query head sharing
+            for j in range(max_len):
+                if j >= lens[b]:
+                    assert out[b, h, j] == -np.inf          # not written
+                    continue
+                slot = start[b] + j
+                if slot >= n_slots:
+                    assert np.isnan(out[b, h, j])
+                    continue
+                ref = float(np.dot(q[b, h].astype(np.float64), kdeq[slot, kv]))
+                tol = 1e-13 * float(np.dot(np.abs(q[b, h]), np.abs(kdeq[slot, kv])))
+                assert abs(out[b, h, j] - ref) <= tol, (b, h, j)
+
+
+def test_decode_scores_bf16_queries_read_as_bf16(orc):
+    import torch
+    rng = _rng(61)
+    codes, scales = _random_cache(rng, 10, 1, 64, 64)
+    qf = rng.standard_normal((1, 1, 64)).astype(np.float32)
+    qb = torch.from_numpy(qf).to(torch.bfloat16)
+    qbits = qb.view(torch.int16).numpy().view(np.uint16)
+    a = orc.decode_scores(orc.shape(1, 1, 64, 5e5), qbits, codes, scales, 64, np.zeros(1, np.int64),
+                          np.array([10], np.int32), 10)
+    b = orc.decode_scores(orc.shape(1, 1, 64, 5e5), qb.float().numpy(), codes, scales, 64, np.zeros(1, np.int64),
+                          np.array([10], np.int32), 10)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("b,g", [(128, 128), (2, 64), (128, 8)])
+def test_decode_scores_approximate_exact_rope_logits(orc, b, g):
+    """Cache written by the rotate path: the logit of the rotated query against
+    the quantised rotated key is the plain RoPE logit (the rotation cancels) up
+    to the quantisation error, |err| <= sum_c |q_c| s_h(c) / 2 (+ fp32 rounding of q)."""
+    rng = _rng(62 + b + g)
+    hq, hk, d, T = 4, 2, 128, 40
+    shp = orc.shape(hq, hk, d, 1e6)
+    q_new = (rng.standard_normal((1, hq, d)) * rng.lognormal(0, 1, d)).astype(np.float32)
+    k = (rng.standard_normal((T, hk, d)) * rng.lognormal(0, 1, d)).astype(np.float32)
+    ang = rng.uniform(-math.pi / 4, math.pi / 4, d // 2).astype(np.float32)
+    pos = np.arange(T, dtype=np.int32)
+    cache = orc.rotate_quantize_qk(orc.shape(0, hk, d, 1e6), None, k, pos, ang, b, g)
+    qr = orc.rotate_quantize_qk(shp, q_new, np.zeros((1, hk, d), np.float32), np.array([T - 1], np.int32), ang, b, g)
+    q_rot = qr["q_rot"].astype(np.float32)
+    sc = orc.decode_scores(shp, q_rot, cache["k_codes"], cache["k_scales"], g, np.zeros(1, np.int64),
+                           np.array([T], np.int32), T)
+    inv = orc.inv_freq(1e6, d)
+    s_h = cache["k_scales"].view(np.float16).astype(np.float64)
+    for h in range(hq):
+        kv = h * hk // hq
+        qe = orc.rope_row(q_new[0, h].astype(np.float64), 0, inv, T - 1)
+        for j in range(T):
+            ke = orc.rope_row(k[j, kv].astype(np.float64), 0, inv, j)
+            exact = float(np.dot(qe, ke))
+            bound = float(np.sum(np.abs(q_rot[0, h]) * np.repeat(s_h[j, kv], g) / 2))
+            bound += 2.0 ** -23 * float(np.dot(np.abs(qe), np.abs(ke))) * 8
+            assert abs(sc[0, h, j] - exact) <= bound, (h, j, sc[0, h, j], exact, bound)

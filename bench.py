@@ -33,7 +33,7 @@ METRIC = "Q/K rotate+INT4-quantise tokens/sec and achieved HBM GB/s (% of peak),
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rotate_quantize_prefill128k_traffic.json")
 KERNEL_SOURCES = ["rotation_rope_pair_amd/csrc/rrp_device.hpp", "rotation_rope_pair_amd/csrc/rrp_rotate.hip",
-                  "rotation_rope_pair_amd/csrc/rrp_kernels.hpp"]
+                  "rotation_rope_pair_amd/csrc/rrp_rotate.hpp"]
 
 
 def kernel_source_hash():
@@ -134,6 +134,43 @@ def qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b
     nbytes = w.bytes_per_token(group=g, with_slot=False, with_v=True) * w.n_tokens
     return {"rotate_quantize_qkv_ms": ms, "qkv_bytes_per_launch": nbytes,
             "qkv_hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "qkv_tokens_per_s": w.n_tokens / (ms * 1e-3)}
+
+
+def decode_scores_timing(dev, stream, reps=20):
+    """rrp_decode_scores over the 256-sequence decode batch (Mistral-shaped, 32 / 8
+    heads, d 128, g 64) reading its 256 x 32768-slot KV4 cache: time per launch and
+    algorithmic GB/s (cache rows read + logits written + queries read)."""
+    import numpy as np
+    import torch
+    import rotation_rope_pair_amd as rrp
+    from rotation_rope_pair_amd import workloads as W
+    w = W.WORKLOADS[5]
+    bt = W.make_decode_batch(5)
+    shape = rrp.layer_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.rope_theta)
+    q = to_device_bf16(bt["q"], dev)
+    codes = torch.from_numpy(bt["codes"]).to(dev)
+    scales = torch.from_numpy(bt["scales"].view(np.int16)).to(dev)
+    start = torch.from_numpy(bt["seq_start"]).to(dev)
+    lens = torch.from_numpy(bt["seq_len"]).to(dev)
+    out = torch.empty((len(bt["seq_len"]), w.n_q_heads, bt["max_len"]), dtype=torch.float32, device=dev)
+
+    def launch():
+        rrp.decode_scores(shape, q, codes, scales, group=bt["group"], seq_start=start, seq_len=lens,
+                          max_len=bt["max_len"], scores=out)
+    for _ in range(3):
+        launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    keys = int(np.minimum(bt["seq_len"], bt["max_len"]).sum())
+    d, hq, hk, g = w.head_dim, w.n_q_heads, w.n_kv_heads, bt["group"]
+    nbytes = keys * hk * (d // 2 + 2 * (d // g)) + keys * hq * 4 + len(bt["seq_len"]) * (hq * d * 2 + 12)
+    return {"decode_scores_ms": ms, "decode_scores_keys": keys, "decode_scores_bytes": nbytes,
+            "decode_scores_hbm_gbs": nbytes / (ms * 1e-3) / 1e9}
 
 
 def main():
@@ -237,6 +274,7 @@ def main():
     if not args.hot_path_only:
         supporting["decode256_rotate_quantize_us"] = decode_latency_us(dev, stream)
         supporting.update(qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b, g))
+        supporting.update(decode_scores_timing(dev, stream))
 
     out = {
         "metric": METRIC,

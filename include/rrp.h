@@ -185,6 +185,39 @@ int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, 
                           int64_t n_tokens, const float* angles, int32_t support_b, int32_t group,
                           double* stats_out, void* stream);
 
+/* rrp_decode_scores -- decode attention logits read straight from the KV4 cache
+ * (LLM rotation-quantisation notes, section 3.2.1: the head-wise rotation
+ * cancels inside Q K^T, so the rotated query against the rotated key is the
+ * RoPE logit; the Qift page, introduction: decode reads the KV cache and is
+ * memory-bound).  The consumer of what rrp_rotate_quantize_qk writes.
+ *
+ * For sequence b, query head h (key head h / (n_q_heads / n_kv_heads)) and key
+ * j < min(seq_len[b], max_len) at cache slot seq_start[b] + j:
+ *   scores[b][h][j] = sum_c q[b][h][c] * code(slot, kv, c) * s_h(slot, kv, c / group)
+ * (the logit before any 1/sqrt(head_dim) factor; fp32 result, fp32 accumulation
+ * of exact f16 products on the matrix cores).
+ *
+ * shape       host; n_q_heads a multiple of n_kv_heads, at most 16 query heads
+ *             per key head (else RRP_ERR_UNSUPPORTED); head_dim 64 or 128.
+ * dtype       dtype of q: RRP_BF16 or RRP_F32.
+ * q           [n_seqs][n_q_heads][head_dim] rotated queries (the q_out of
+ *             rrp_rotate_quantize_qk for the decode tokens), 16-byte aligned.
+ * k_codes     uint8 [n_slots][n_kv_heads][head_dim/2], 4-byte aligned.
+ * k_scales    uint16 fp16 bits [n_slots][n_kv_heads][head_dim/group], aligned to
+ *             min(2 * head_dim/group, 8) bytes.
+ * group       the group size the cache was written with (power of two in [2, head_dim]).
+ * seq_start   int64[n_seqs], 8-byte aligned: slot of key 0 of each sequence.
+ * seq_len     int32[n_seqs]: keys per sequence (values above max_len are cut to max_len).
+ * max_len     row length of `scores`.
+ * scores      fp32 [n_seqs][n_q_heads][max_len].  Only j < min(seq_len[b], max_len)
+ *             is written; a key whose slot lies outside [0, n_slots) gets NaN.
+ * n_slots     cache capacity in slots, >= 1.
+ * n_seqs == 0 or max_len == 0 is a no-op returning RRP_OK. */
+int rrp_decode_scores(const rrp_shape* shape, int32_t dtype, const void* q, int64_t n_seqs,
+                      const uint8_t* k_codes, const uint16_t* k_scales, int32_t group, int64_t n_slots,
+                      const int64_t* seq_start, const int32_t* seq_len, int32_t max_len, float* scores,
+                      void* stream);
+
 /* Host: static description of a status code. */
 const char* rrp_status_string(int status);
 

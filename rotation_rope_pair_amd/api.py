@@ -169,6 +169,29 @@ def quant_error_stats(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, su
     _abi.check("rrp_quant_error_stats", L.rrp_quant_error_stats(*args))
 
 
-__all__ = ["layer_shape", "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
+def decode_scores(shape: RrpShape, q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, *, group: int,
+                  seq_start: torch.Tensor, seq_len: torch.Tensor, max_len: int, scores: torch.Tensor,
+                  n_slots: Optional[int] = None, stream=None) -> None:
+    """Enqueue rrp_decode_scores: decode logits of the rotated queries q
+    [n_seqs][Hq][d] against the KV4 cache into scores fp32 [n_seqs][Hq][max_len]
+    (see include/rrp.h)."""
+    L = _abi.load()
+    d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    B = int(seq_len.numel())
+    dev = q.device
+    if n_slots is None:
+        n_slots = int(k_codes.shape[0])
+    ng = max(1, d // max(1, int(group)))
+    args = [
+        ctypes.byref(shape), _dtype_code(q), _dev(q, "q", B * hq * d, q.dtype, dev), B,
+        _dev(k_codes, "k_codes", n_slots * hk * (d // 2), torch.uint8, dev),
+        _dev(k_scales, "k_scales", n_slots * hk * ng, (torch.float16, torch.int16), dev), int(group), int(n_slots),
+        _dev(seq_start, "seq_start", B, torch.int64, dev), _dev(seq_len, "seq_len", B, torch.int32, dev),
+        int(max_len), _dev(scores, "scores", B * hq * int(max_len), torch.float32, dev), _stream_ptr(stream, dev),
+    ]
+    _abi.check("rrp_decode_scores", L.rrp_decode_scores(*args))
+
+
+__all__ = ["layer_shape", "decode_scores", "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
            "new_moments", "RrpError", "RrpShape", "ESTIMATORS", "RRP_F32", "RRP_BF16",
            "RRP_ROPE_HALF_SPLIT", "RRP_ROPE_INTERLEAVED"]

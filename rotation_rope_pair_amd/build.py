@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librrp.so")
-SOURCES = ["rrp_abi.hip", "rrp_rotate.hip", "rrp_calib.hip", "rrp_stats.hip"]
+SOURCES = ["rrp_abi.hip", "rrp_rotate.hip", "rrp_calib.hip", "rrp_stats.hip", "rrp_decode.hip"]
 ARCH = os.environ.get("RRP_OFFLOAD_ARCH", "gfx950")
 
 

@@ -236,3 +236,43 @@ RRP_EXPORT int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, cons
     }
     return rrp::launch_stats_final(f, s) == hipSuccess ? RRP_OK : RRP_ERR_HIP;
 }
+
+RRP_EXPORT int rrp_decode_scores(const rrp_shape* shape, int32_t dtype, const void* q, int64_t n_seqs,
+                                 const uint8_t* k_codes, const uint16_t* k_scales, int32_t group, int64_t n_slots,
+                                 const int64_t* seq_start, const int32_t* seq_len, int32_t max_len, float* scores,
+                                 void* stream) {
+    int st = check_shape(shape, dtype);
+    if (st != RRP_OK) return st;
+    const int hq = shape->n_q_heads, hk = shape->n_kv_heads, d = shape->head_dim;
+    if (hq < 1 || hq % hk != 0) return RRP_ERR_INVALID_ARG;
+    if (hq / hk > 16) return RRP_ERR_UNSUPPORTED;  // one MFMA column per query head of a key head
+    if (!is_pow2(group) || group < 2 || group > d) return RRP_ERR_INVALID_ARG;
+    if (n_seqs < 0 || n_slots < 0 || max_len < 0) return RRP_ERR_INVALID_ARG;
+    if (n_seqs == 0 || max_len == 0) return RRP_OK;
+    if (n_slots == 0) return RRP_ERR_INVALID_ARG;  // an empty cache holds no key to read
+    if (q == nullptr || k_codes == nullptr || k_scales == nullptr || seq_start == nullptr || seq_len == nullptr ||
+        scores == nullptr)
+        return RRP_ERR_INVALID_ARG;
+    const uintptr_t scale_align = 2 * (d / group) < 8 ? 2 * (d / group) : 8;
+    if (!aligned(q, 16) || !aligned(k_codes, 4) || !aligned(k_scales, scale_align) || !aligned(seq_start, 8) ||
+        !aligned(seq_len, 4) || !aligned(scores, 4))
+        return RRP_ERR_MISALIGNED;
+    rrp::DecodeArgs a{};
+    a.q = q;
+    a.k_codes = k_codes;
+    a.k_scales = k_scales;
+    a.seq_start = seq_start;
+    a.seq_len = seq_len;
+    a.scores = scores;
+    a.n_seqs = n_seqs;
+    a.n_slots = n_slots;
+    a.n_chunks = rrp::decode_chunks(max_len);
+    a.hq = hq;
+    a.hk = hk;
+    a.group_heads = hq / hk;
+    a.max_len = max_len;
+    a.vec_store = (max_len % 4 == 0 && aligned(scores, 16)) ? 1 : 0;
+    if ((n_seqs * a.n_chunks * hk + 3) / 4 > 0x7FFFFFFF) return RRP_ERR_INVALID_ARG;  // grid too large
+    const hipError_t e = rrp::launch_decode_scores(a, dtype, d, group, (hipStream_t)stream);
+    return e == hipSuccess ? RRP_OK : RRP_ERR_HIP;
+}

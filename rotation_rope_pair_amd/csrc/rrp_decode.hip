@@ -1,0 +1,407 @@
+// rrp_decode.hip -- decode attention logits straight from the KV4 cache.
+//
+// score[b][h][j] = sum_c q[b][h][c] * code(slot, kv, c) * s_h(slot, kv, c / g)
+// for key j of sequence b at slot seq_start[b] + j, key head kv = h / (Hq / Hkv).
+//
+// One wavefront takes one (sequence, key head, chunk of kKeysPerWave keys).  The
+// contraction over channels runs on the matrix cores: v_mfma_f32_16x16x32_f16
+// with A = 16 keys x 32 channels of INT4 codes turned into f16 (exact small
+// integers) and B = 32 channels x 16 columns holding the Hq / Hkv query heads
+// that share the key head (f16, each head scaled by a power of two so that its
+// largest value sits just below 2^15; fp32 queries as a hi + lo pair of f16
+// terms).  Products of f16 values are exact in the fp32 accumulator.  Each MFMA
+// covers 32 consecutive channels; the group scales (fp16 -> fp32) multiply the
+// per-group partial sums in fp32, so the codes never meet a rounded scale.
+//
+// Lane roles (16x16x32 layout): A row i = lane % 16 (key), k block kb = lane / 16
+// (8 channels); B column j = lane % 16 (query head); D holds keys 4 * (lane / 16)
+// + r, r = 0..3, of column lane % 16.  Inside a lane's 8 channels the element order
+// is (0, 4, 1, 5, 2, 6, 3, 7): that is the order in which the nibble-to-f16
+// conversion produces them, and B is laid out the same way.
+#include <type_traits>
+
+#include "rrp_device.hpp"
+#include "rrp_kernels.hpp"
+
+namespace rrp {
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#ifndef RRP_DECODE_KEYS_PER_WAVE
+#define RRP_DECODE_KEYS_PER_WAVE 256
+#endif
+constexpr int kKeysPerWave = RRP_DECODE_KEYS_PER_WAVE;
+#ifndef RRP_DECODE_TILES_PER_STEP
+#define RRP_DECODE_TILES_PER_STEP 4
+#endif
+constexpr int kTilesPerStep = RRP_DECODE_TILES_PER_STEP;  // 16-key tiles loaded per step
+
+// Channel offset (inside a lane's 8 channels) of half8 element e.
+__device__ __forceinline__ constexpr int elem_channel(int e) { return (e >> 1) + 4 * (e & 1); }
+
+// Eight two's-complement INT4 codes (nibble n = channel n) -> half8 in element order.
+// Offset binary (x ^ 8) under the f16 exponent of 1024 gives 1024 + code + 8
+// exactly; subtracting 1032 leaves the code.
+__device__ __forceinline__ half8 codes_to_half8(unsigned w) {
+    const unsigned x = w ^ 0x88888888u;
+    const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    half8 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const unsigned bits = ((x >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
+        const half2v h = __builtin_bit_cast(half2v, bits) - off;
+        r[2 * p] = h[0];
+        r[2 * p + 1] = h[1];
+    }
+    return r;
+}
+
+// Zero the elements of a half8 whose channel (8 * kb + elem_channel(e)) is not in
+// sub-group u of size GS (GS < 32).
+template <int GS>
+__device__ __forceinline__ half8 mask_subgroup(half8 a, int kb, int u) {
+    half8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = ((8 * kb + elem_channel(e)) / GS == u) ? a[e] : (_Float16)0.0f;
+    return r;
+}
+
+template <typename E> struct QLoad;
+template <> struct QLoad<bf16_tag> {
+    // 8 consecutive channels of a bf16 row -> fp32
+    __device__ static void load(const void* row, int c0, float (&x)[8]) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + c0);
+        float t[8];
+        unpack_chunk<bf16_tag, 8>(w, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = t[e];
+    }
+};
+template <> struct QLoad<float> {
+    __device__ static void load(const void* row, int c0, float (&x)[8]) {
+        const float* p = static_cast<const float*>(row) + c0;
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(p + 4);
+        x[0] = __uint_as_float(w0.x); x[1] = __uint_as_float(w0.y);
+        x[2] = __uint_as_float(w0.z); x[3] = __uint_as_float(w0.w);
+        x[4] = __uint_as_float(w1.x); x[5] = __uint_as_float(w1.y);
+        x[6] = __uint_as_float(w1.z); x[7] = __uint_as_float(w1.w);
+    }
+};
+
+// Largest of v over the four lanes l, l + 16, l + 32, l + 48.
+__device__ __forceinline__ float max_over_kb(float v) {
+    const int lane = (int)__lane_id();
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 16) << 2, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(v))));
+    return v;
+}
+
+template <typename E, int D, int GS>
+__global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) {
+    constexpr int NM = D / 32;                                  // MFMAs per 16-key tile
+    constexpr int NG = D / GS;                                  // groups per key row
+    constexpr int SPLIT = ElemInfo<E>::bytes == 4 ? 2 : 1;      // f16 terms per query value
+    constexpr int SROW = NG * 2;                                // scale bytes per key row
+
+    const int lane = (int)__lane_id();
+    const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int hk = a.hk;
+    const int kvh = (int)(wid % hk);
+    const int64_t rest = wid / hk;
+    const int chunk = (int)(rest % a.n_chunks);
+    const int64_t b = rest / a.n_chunks;
+    if (b >= a.n_seqs) return;
+    int len = a.seq_len[b];
+    len = len < a.max_len ? len : a.max_len;
+    const int k_begin = chunk * kKeysPerWave;
+    if (k_begin >= len) return;                                 // uniform per wave
+    const int k_end = min(len, k_begin + kKeysPerWave);
+    const int64_t start = a.seq_start[b];
+
+    const int col = lane & 15;  // A row (key in tile) / B and D column (query head)
+    const int kb = lane >> 4;   // A / B channel block; D key quad
+    const int G = a.group_heads;
+    const bool head_ok = col < G;
+    const int h = kvh * G + col;
+
+    const unsigned char* codes = a.k_codes;
+    const unsigned char* scales = reinterpret_cast<const unsigned char*>(a.k_scales);
+    const size_t code_row = (size_t)D / 2, scale_row = SROW;
+    const size_t slot_stride_c = (size_t)hk * code_row, slot_stride_s = (size_t)hk * scale_row;
+    const unsigned char* codes_h = codes + (size_t)kvh * code_row + 4 * kb;
+    const unsigned char* scales_h = scales + (size_t)kvh * scale_row;
+    // Every key of this wave's chunk sits inside the cache (the usual case):
+    // keys are then only clamped to the chunk, with no 64-bit range checks.
+    const bool chunk_in_cache = start + k_begin >= 0 && start + k_end <= a.n_slots;
+
+    auto body = [&](auto in_cache_tag) {
+        constexpr bool FAST = decltype(in_cache_tag)::value;
+        // Row address of `key` inside a half-row base (codes or scales), and whether
+        // the key is real.  Loads are issued unconditionally from a valid address
+        // and zeroed afterwards, so no branch separates them and the waits stay
+        // exact.
+        const unsigned char* codes_s = codes_h + (FAST ? start * (int64_t)slot_stride_c : 0);
+        const unsigned char* scales_s = scales_h + (FAST ? start * (int64_t)slot_stride_s : 0);
+        auto row_of = [&](int key, bool scale_half, bool& ok) -> const unsigned char* {
+            const size_t stride = scale_half ? slot_stride_s : slot_stride_c;
+            if constexpr (FAST) {
+                ok = key < k_end;
+                const int kc = min(key, k_end - 1);
+                return (scale_half ? scales_s : codes_s) + (size_t)(unsigned)kc * stride;
+            } else {
+                const int64_t slot = start + key;
+                ok = key < k_end && slot >= 0 && slot < a.n_slots;
+                return (scale_half ? scales_h : codes_h) + (size_t)(ok ? slot : 0) * stride;
+            }
+        };
+
+        // A loads for the tile starting at key0: NM words (8 codes each) of key key0 + col.
+        auto load_a = [&](int key0, unsigned (&w)[NM]) {
+            bool ok;
+            const unsigned char* row = row_of(key0 + col, false, ok);
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                w[m] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(row + 16 * m));
+            if (!FAST || key0 + 16 > k_end) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m) w[m] = ok ? w[m] : 0u;
+            }
+        };
+        // Scales of groups [g0, g0 + NS) of the lane's four D keys key0 + 4 kb + r, as fp32.
+        auto load_s = [&](int key0, int g0, auto& sv) {
+            constexpr int NS = sizeof(sv[0]) / sizeof(float);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                bool ok;
+                const unsigned char* row = row_of(key0 + 4 * kb + r, true, ok) + 2 * g0;
+                if constexpr (NS == 1) {
+                    unsigned short v = *reinterpret_cast<const unsigned short*>(row);
+                    v = ok ? v : (unsigned short)0;
+                    sv[r][0] = f16_bits_to_f32(v);
+                } else if constexpr (NS == 2) {
+                    unsigned v = *reinterpret_cast<const unsigned*>(row);
+                    v = ok ? v : 0u;
+                    sv[r][0] = f16_bits_to_f32(v & 0xFFFFu);
+                    sv[r][1] = f16_bits_to_f32(v >> 16);
+                } else {
+#pragma unroll
+                    for (int q4 = 0; q4 < NS / 4; ++q4) {
+                        u32x2 v = *reinterpret_cast<const u32x2*>(row + 8 * q4);
+                        v = ok ? v : u32x2{0u, 0u};
+                        sv[r][4 * q4 + 0] = f16_bits_to_f32(v.x & 0xFFFFu);
+                        sv[r][4 * q4 + 1] = f16_bits_to_f32(v.x >> 16);
+                        sv[r][4 * q4 + 2] = f16_bits_to_f32(v.y & 0xFFFFu);
+                        sv[r][4 * q4 + 3] = f16_bits_to_f32(v.y >> 16);
+                    }
+                }
+            }
+        };
+
+        // Groups of at least 32 channels: the key's whole scale row (<= 8 bytes) is
+        // loaded with its codes, kept as raw fp16 words until used.  Smaller groups:
+        // each MFMA's scales are read when it is used.
+        constexpr int NSW = GS >= 32 ? (SROW + 3) / 4 : 1;
+        auto load_sw = [&](int key0, unsigned (&sw)[4][NSW]) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                bool ok;
+                const unsigned char* row = row_of(key0 + 4 * kb + r, true, ok);
+                if constexpr (SROW == 2) {
+                    const unsigned v = *reinterpret_cast<const unsigned short*>(row);
+                    sw[r][0] = ok ? v : 0u;
+                } else if constexpr (SROW == 4) {
+                    const unsigned v = *reinterpret_cast<const unsigned*>(row);
+                    sw[r][0] = ok ? v : 0u;
+                } else {
+                    const u32x2 v = *reinterpret_cast<const u32x2*>(row);
+                    sw[r][0] = ok ? v.x : 0u;
+                    sw[r][1] = ok ? v.y : 0u;
+                }
+            }
+        };
+
+        // Steps of kTilesPerStep tiles; the next step's codes and scales are in
+        // flight while the current step is computed.
+        constexpr int TP = kTilesPerStep;
+        unsigned wc[TP][NM], wn[TP][NM];
+        unsigned sc[TP][4][NSW], sn[TP][4][NSW];
+        auto load_step = [&](int s0, unsigned (&w)[TP][NM], unsigned (&sw)[TP][4][NSW]) {
+#pragma unroll
+            for (int tt = 0; tt < TP; ++tt) {
+                load_a(s0 + 16 * tt, w[tt]);
+                if constexpr (GS >= 32) load_sw(s0 + 16 * tt, sw[tt]);
+            }
+        };
+        load_step(k_begin, wc, sc);  // the first codes are in flight while the queries are prepared
+
+        // ---- B operand: this lane's query channels 32 m + 8 kb + elem_channel(e) ----
+        float qv[NM][8];
+        float qmax = 0.0f;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            float x[8];
+            if (head_ok) {
+                const void* row = static_cast<const unsigned char*>(a.q) +
+                                  ((size_t)b * a.hq + h) * D * ElemInfo<E>::bytes;
+                QLoad<E>::load(row, 32 * m + 8 * kb, x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qv[m][e] = x[elem_channel(e)];
+                qmax = fmaxf(qmax, fabsf(qv[m][e]));
+            }
+        }
+        qmax = max_over_kb(qmax);
+        // power of two that brings the head's largest magnitude into [2^14, 2^15)
+        const int qexp = (qmax > 0.0f && qmax <= 3.4e38f) ? 14 - ilogbf(qmax) : 0;
+        half8 bq[SPLIT][NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = ldexpf(qv[m][e], qexp);
+                const _Float16 hi = (_Float16)v;
+                bq[0][m][e] = hi;
+                if constexpr (SPLIT == 2) bq[SPLIT - 1][m][e] = (_Float16)(v - (float)hi);
+            }
+        float* out_row = a.scores + ((size_t)b * a.hq + h) * a.max_len;
+        const float descale = ldexpf(1.0f, -qexp);
+
+        // One 16-key tile: dequantise, contract on the matrix cores, scale, store.
+        auto tile = [&](int key0, const unsigned (&w)[NM], const unsigned (&sw)[4][NSW]) {
+            half8 am[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) am[m] = codes_to_half8(w[m]);
+
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (GS >= 32) {
+                constexpr int MPG = GS / 32;  // MFMAs per group
+#pragma unroll
+                for (int gq = 0; gq < NG; ++gq) {
+                    f32x4 dq = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int m = gq * MPG; m < (gq + 1) * MPG; ++m)
+#pragma unroll
+                        for (int t = 0; t < SPLIT; ++t)
+                            dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(am[m], bq[t][m], dq, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float scl = f16_bits_to_f32((unsigned short)(sw[r][gq >> 1] >> (16 * (gq & 1))));
+                        acc[r] = fmaf(scl, dq[r], acc[r]);
+                    }
+                }
+            } else {
+                constexpr int SUB = 32 / GS;  // groups inside one MFMA
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    if constexpr (SUB <= 2) {
+                        float sm[4][SUB];
+                        load_s(key0, m * SUB, sm);
+#pragma unroll
+                        for (int u = 0; u < SUB; ++u) {
+                            const half8 amu = mask_subgroup<GS>(am[m], kb, u);
+                            f32x4 dq = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                            for (int t = 0; t < SPLIT; ++t)
+                                dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(amu, bq[t][m], dq, 0, 0, 0);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[r] = fmaf(sm[r][u], dq[r], acc[r]);
+                        }
+                    } else {
+                        // many small groups: one sub-group (and its scale) at a time
+#pragma unroll 1
+                        for (int u = 0; u < SUB; ++u) {
+                            float su[4][1];
+                            load_s(key0, m * SUB + u, su);
+                            const half8 amu = mask_subgroup<GS>(am[m], kb, u);
+                            f32x4 dq = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                            for (int t = 0; t < SPLIT; ++t)
+                                dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(amu, bq[t][m], dq, 0, 0, 0);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[r] = fmaf(su[r][0], dq[r], acc[r]);
+                        }
+                    }
+                }
+            }
+
+            if (head_ok) {
+                const int kq = key0 + 4 * kb;  // this lane's four consecutive keys
+                f32x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (FAST) {
+                        o[r] = acc[r] * descale;
+                    } else {
+                        const int64_t slot = start + kq + r;
+                        o[r] = (slot >= 0 && slot < a.n_slots) ? acc[r] * descale : __builtin_nanf("");
+                    }
+                }
+                if (a.vec_store && kq + 3 < k_end) {
+                    __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out_row + kq));
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (kq + r < k_end) __builtin_nontemporal_store(o[r], out_row + kq + r);
+                }
+            }
+        };
+
+        for (int s0 = k_begin; s0 < k_end; s0 += 16 * TP) {
+            if (s0 + 16 * TP < k_end) load_step(s0 + 16 * TP, wn, sn);
+#pragma unroll
+            for (int tt = 0; tt < TP; ++tt)
+                if (s0 + 16 * tt < k_end) tile(s0 + 16 * tt, wc[tt], sc[tt]);
+#pragma unroll
+            for (int tt = 0; tt < TP; ++tt) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m) wc[tt][m] = wn[tt][m];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int x = 0; x < NSW; ++x) sc[tt][r][x] = sn[tt][r][x];
+            }
+        }
+    };
+    if (chunk_in_cache) body(std::true_type{});
+    else body(std::false_type{});
+}
+
+template <typename E, int D>
+hipError_t launch_d(const DecodeArgs& a, int group, hipStream_t st) {
+    const int64_t waves = a.n_seqs * a.n_chunks * a.hk;
+    const int64_t blocks = (waves + 3) / 4;
+    const dim3 grid((unsigned)blocks), block(256);
+#define RRP_G(GS) \
+    if (group == GS) { hipLaunchKernelGGL((decode_scores_kernel<E, D, GS>), grid, block, 0, st, a); return hipGetLastError(); }
+    RRP_G(2) RRP_G(4) RRP_G(8) RRP_G(16) RRP_G(32) RRP_G(64)
+    if constexpr (D >= 128) { RRP_G(128) }
+#undef RRP_G
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int64_t decode_chunks(int max_len) { return (max_len + kKeysPerWave - 1) / kKeysPerWave; }
+
+hipError_t launch_decode_scores(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t st) {
+    if (dtype == 1) {
+        if (head_dim == 64) return launch_d<bf16_tag, 64>(a, group, st);
+        if (head_dim == 128) return launch_d<bf16_tag, 128>(a, group, st);
+    } else {
+        if (head_dim == 64) return launch_d<float, 64>(a, group, st);
+        if (head_dim == 128) return launch_d<float, 128>(a, group, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace rrp

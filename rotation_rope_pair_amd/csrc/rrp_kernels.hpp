@@ -4,42 +4,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rrp_rotate.hpp"
+
 namespace rrp {
 
-constexpr int kMaxPairs = 64;        // head_dim <= 128
 constexpr int kMaxCalibBlocks = 4096;  // block partials of the calibration pass
 constexpr int kMaxStatsBlocks = 4096;  // block partials of the diagnostic pass
-
-// RoPE frequencies travel in the kernel argument block: every lane reads its
-// own pair's entry, so no device table has to be allocated or kept.
-struct RotateArgs {
-    const void* q;
-    const void* k;
-    const int32_t* pos;
-    const float* angles;
-    void* q_out;
-    uint8_t* k_codes;
-    uint16_t* k_scales;
-    const int64_t* slot_mapping;
-    float* q_dbg;
-    float* k_dbg;
-    float* s_dbg;
-    const void* v;       // NULL: no V rows
-    uint8_t* v_codes;
-    uint16_t* v_scales;
-    float* v_dbg;
-    float* vs_dbg;
-    int64_t n_tokens;
-    int64_t n_slots;
-    int32_t hq;       // Q heads in the tensor layout
-    int32_t hq_rows;  // Q rows processed per token (0 when Q is skipped)
-    int32_t hk;
-    int32_t support_b;
-    int32_t group;
-    double rsqrt_b;
-    double rsqrt_v;  // 1 / sqrt(head_dim)
-    float inv_freq[kMaxPairs];
-};
 
 struct CalibArgs {
     const void* q;
@@ -87,8 +57,23 @@ struct StatsFinalArgs {
     double n_rows;
 };
 
-// dtype: 0 fp32, 1 bf16; layout: 0 half-split, 1 interleaved.
-hipError_t launch_rotate_quantize(const RotateArgs& a, int dtype, int head_dim, int layout, hipStream_t st);
+struct DecodeArgs {
+    const void* q;             // [n_seqs][hq][head_dim] rotated queries
+    const uint8_t* k_codes;    // [n_slots][hk][head_dim / 2]
+    const uint16_t* k_scales;  // [n_slots][hk][head_dim / group] fp16 bits
+    const int64_t* seq_start;  // [n_seqs] slot of key 0
+    const int32_t* seq_len;    // [n_seqs] keys per sequence
+    float* scores;             // [n_seqs][hq][max_len]
+    int64_t n_seqs;
+    int64_t n_slots;
+    int64_t n_chunks;          // key chunks per sequence (one wave each)
+    int32_t hq;
+    int32_t hk;
+    int32_t group_heads;       // hq / hk query heads per key head
+    int32_t max_len;
+    int32_t vec_store;         // scores rows are 16-byte aligned: store 4 logits at once
+};
+
 
 int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int* nbq, int* nbk);
 hipError_t launch_calibrate(const CalibArgs& a, int dtype, int head_dim, int layout, hipStream_t st);
@@ -97,5 +82,8 @@ hipError_t launch_calibrate_final(const CalibFinalArgs& a, hipStream_t st);
 int stats_blocks(int64_t n_tokens);
 hipError_t launch_stats(const StatsArgs& a, int n_blocks, int dtype, int head_dim, int layout, hipStream_t st);
 hipError_t launch_stats_final(const StatsFinalArgs& a, hipStream_t st);
+
+int64_t decode_chunks(int max_len);
+hipError_t launch_decode_scores(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t st);
 
 }  // namespace rrp

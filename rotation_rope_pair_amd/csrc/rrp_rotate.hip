@@ -15,7 +15,7 @@
 // streaming (non-temporal) hints: the kernel is bound by HBM bandwidth and by
 // the vector ALU.
 #include "rrp_device.hpp"
-#include "rrp_kernels.hpp"
+#include "rrp_rotate.hpp"
 
 namespace rrp {
 

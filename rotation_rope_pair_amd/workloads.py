@@ -191,3 +191,28 @@ def make_inputs(number: int, n_tokens: Optional[int] = None, want_q: bool = True
             "k": _draw_samples((seed, 5), w, pk, Tc),
         }
     return res
+
+
+def make_decode_batch(number: int = 5, group: Optional[int] = None):
+    """Decode attention batch over a filled KV4 cache for the decode workload:
+    one query token per sequence (the workload's Q rows stand in for the rotated
+    queries), sequence b owning slots [b * C, (b + 1) * C) with C the position
+    range, and its new token at position p_b attending to keys 0..p_b
+    (seq_len = p_b + 1).  The cache holds seeded random code bytes (every nibble
+    is a valid two's-complement INT4 code) and fp16 scales 2^U(-8, 3); streams 8
+    and 9 of the workload seed.  Returns dict(q, codes, scales, seq_start,
+    seq_len, n_slots, max_len, group)."""
+    w = WORKLOADS[number]
+    if not w.decode_positions:
+        raise ValueError("workload has no decode batch")
+    g = group or w.group
+    inp = make_inputs(number)
+    B, C, hk, d = w.n_tokens, w.decode_positions, w.n_kv_heads, w.head_dim
+    n_slots = B * C
+    seed = 1000 + number
+    codes = _rng(seed, 8).integers(0, 256, size=(n_slots, hk, d // 2), dtype=np.uint8)
+    expo = _rng(seed, 9).uniform(-8.0, 3.0, size=(n_slots, hk, d // g))
+    scales = np.exp2(expo).astype(np.float16).view(np.uint16)
+    return {"q": inp["q"], "codes": codes, "scales": scales,
+            "seq_start": (np.arange(B, dtype=np.int64) * C), "seq_len": (inp["pos"].astype(np.int32) + 1),
+            "n_slots": n_slots, "max_len": C, "group": g}

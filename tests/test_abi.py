@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["rrp_calibrate_angles", "rrp_quant_error_stats", "rrp_rotate_quantize_qk",
-                                           "rrp_rotate_quantize_qkv", "rrp_status_string", "rrp_version"])
+                                           "rrp_rotate_quantize_qkv", "rrp_decode_scores", "rrp_status_string",
+                                           "rrp_version"])
 
 
 def test_library_exports_exactly_the_declared_symbols(lib):
@@ -94,6 +95,24 @@ def test_rotate_qkv_validation(lib):
     assert rqkv(v=None) == 1 and rqkv(vc=None) == 1 and rqkv(vs=None) == 1 and rqkv(k=None) == 1
     assert rqkv(v=P2) == 2 and rqkv(vc=P2) == 2 and rqkv(vd=P2) == 2
     assert rqkv(vs=ctypes.c_void_p((1 << 20) + 1)) == 2
+
+
+def test_decode_scores_validation(lib):
+    def dec(shape=None, dtype=1, q=P16, B=4, codes=P16, scales=P16, g=64, n_slots=100, start=P16, lens=P16,
+            max_len=64, out=P16):
+        return lib.rrp_decode_scores(ctypes.byref(shape or _shape()), dtype, q, B, codes, scales, g, n_slots, start,
+                                     lens, max_len, out, None)
+    assert dec(B=0) == 0 and dec(max_len=0) == 0                  # nothing to do
+    assert dec(shape=_shape(hq=12, hk=8)) == 1                    # query heads not a multiple of key heads
+    assert dec(shape=_shape(hq=0)) == 1
+    assert dec(shape=_shape(hq=32, hk=1)) == 3                    # more than 16 query heads per key head
+    assert dec(g=3) == 1 and dec(g=256) == 1 and dec(g=1) == 1
+    assert dec(B=-1) == 1 and dec(n_slots=-1) == 1 and dec(max_len=-5) == 1 and dec(n_slots=0) == 1
+    assert dec(q=None) == 1 and dec(codes=None) == 1 and dec(scales=None) == 1
+    assert dec(start=None) == 1 and dec(lens=None) == 1 and dec(out=None) == 1
+    assert dec(q=P2) == 2 and dec(codes=P2) == 2 and dec(start=ctypes.c_void_p((1 << 20) + 4)) == 2
+    assert dec(scales=ctypes.c_void_p((1 << 20) + 2), g=32) == 2   # 8-byte scale rows need 8-byte alignment
+    assert dec(shape=_shape(d=96)) == 3
 
 
 def test_calibrate_validation(lib):

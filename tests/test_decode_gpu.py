@@ -1,0 +1,205 @@
+"""GPU parity of rrp_decode_scores (decode logits read from the KV4 cache).
+
+The cache and the rotated queries given to the kernel are written by the
+oracle (small cases) or drawn by the seeded generator (the full decode batch);
+the same bytes go to the oracle's decode-score function.  Tolerance: the GPU
+accumulates exact f16 products in fp32, so each logit may differ from the fp64
+value by a few fp32 roundings of the running sum: |err| <= 1e-5 * sum_c |q_c k_c|
+(fp32 queries are carried as a hi + lo pair of f16 terms, 2^-22 relative).
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+import rotation_rope_pair_amd as rrp  # noqa: E402
+from rotation_rope_pair_amd import workloads as W  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU-only container
+    pytest.skip("no GPU", allow_module_level=True)
+
+DEV = torch.device("cuda:0")
+REL_TOL = 1e-5
+
+
+def to_dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def to_dev_q(q):
+    if q.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(q).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(q)).to(DEV)
+
+
+def unpack(codes):
+    lo = (codes & 0xF).astype(np.int8)
+    hi = (codes >> 4).astype(np.int8)
+    lo = np.where(lo > 7, lo - 16, lo)
+    hi = np.where(hi > 7, hi - 16, hi)
+    return np.stack([lo, hi], -1).reshape(*codes.shape[:-1], 2 * codes.shape[-1])
+
+
+def q_values(q):
+    if q.dtype == np.uint16:
+        return (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return q.astype(np.float64)
+
+
+def run_gpu(shp, q, codes, scales, g, start, lens, max_len, n_slots=None):
+    B = len(lens)
+    out = torch.full((B, shp.n_q_heads, max_len), float("-inf"), dtype=torch.float32, device=DEV)
+    rrp.decode_scores(shp, to_dev_q(q), to_dev(codes), to_dev(scales), group=g, seq_start=to_dev(start),
+                      seq_len=to_dev(lens), max_len=max_len, scores=out, n_slots=n_slots)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def magnitude(q, codes, scales, g, start, lens, max_len, hq, hk, seqs):
+    """sum_c |q_c k_c| for every written logit of the given sequences (for the
+    tolerance), dequantising only those sequences' cache rows."""
+    qv = q_values(q)
+    mags = {}
+    for b in seqs:
+        n = min(int(lens[b]), max_len)
+        sl = np.clip(start[b] + np.arange(n), 0, codes.shape[0] - 1)
+        kdeq = np.abs(unpack(codes[sl]).astype(np.float64) *
+                      np.repeat(scales[sl].view(np.float16).astype(np.float64), g, axis=-1))
+        for h in range(hq):
+            kv = h * hk // hq
+            mags[(b, h)] = kdeq[:, kv] @ np.abs(qv[b, h])
+    return mags
+
+
+def compare(got, ref, mags, seqs, hq, lens, max_len):
+    worst = 0.0
+    for b in seqs:
+        n = min(int(lens[b]), max_len)
+        assert np.all(np.isneginf(got[b, :, n:])), "wrote past the sequence length"
+        for h in range(hq):
+            g_, r_ = got[b, h, :n].astype(np.float64), ref[b, h, :n]
+            nan = np.isnan(r_)
+            assert np.array_equal(np.isnan(g_), nan), (b, h)
+            err = np.abs(g_[~nan] - r_[~nan])
+            lim = REL_TOL * np.maximum(mags[(b, h)][~nan], 1e-300)
+            assert np.all(err <= lim), (b, h, float((err / lim).max()))
+            if err.size:
+                worst = max(worst, float((err / np.maximum(mags[(b, h)][~nan], 1e-300)).max()))
+    return worst
+
+
+@pytest.mark.parametrize("dtype,d,hq,hk,g", [
+    ("bf16", 128, 32, 8, 64), ("bf16", 128, 32, 8, 128), ("bf16", 64, 32, 8, 64), ("f32", 64, 2, 1, 64),
+    ("bf16", 128, 16, 1, 32), ("f32", 128, 6, 2, 16), ("bf16", 64, 4, 4, 8), ("bf16", 128, 8, 2, 4),
+    ("f32", 64, 4, 2, 2)])
+def test_decode_scores_against_oracle_cache(dtype, d, hq, hk, g):
+    """Cache and queries written by the oracle's rotate path; ragged lengths across
+    tile and chunk edges, an empty sequence, keys past the cache (NaN), and a row
+    length that is not a multiple of 4."""
+    rng = np.random.Generator(np.random.PCG64(900 + d + hq + g))
+    lens = np.array([0, 1, 15, 16, 17, 255, 256, 257, 600, 37], np.int32)
+    B, cap = len(lens), 640
+    n_slots = B * cap
+    start = np.arange(B, dtype=np.int64) * cap
+    start[-1] = n_slots - 20                     # the last sequence runs past the cache
+    max_len = 603
+    shp = O.shape(hq, hk, d, 1e6)
+    k = (rng.standard_normal((n_slots, hk, d)) * rng.lognormal(0, 1, d)).astype(np.float32)
+    qraw = (rng.standard_normal((B, hq, d)) * rng.lognormal(0, 1, d)).astype(np.float32)
+    if dtype == "bf16":
+        k = W._to_storage(k, "bf16")
+        qraw = W._to_storage(qraw, "bf16")
+    ang = rng.uniform(-math.pi / 4, math.pi / 4, d // 2).astype(np.float32)
+    pos = (np.arange(n_slots) % cap).astype(np.int32)
+    cache = O.rotate_quantize_qk(O.shape(0, hk, d, 1e6), None, k, pos, ang, d, g)
+    qo = O.rotate_quantize_qk(shp, qraw, np.zeros((B, hk, d), qraw.dtype), lens.clip(0), ang, d, g)["q_out"]
+    ref = O.decode_scores(shp, qo, cache["k_codes"], cache["k_scales"], g, start, lens, max_len)
+    got = run_gpu(rrp.layer_shape(hq, hk, d, 1e6), qo, cache["k_codes"], cache["k_scales"], g, start, lens, max_len)
+    mags = magnitude(qo, cache["k_codes"], cache["k_scales"], g, start, lens, max_len, hq, hk, range(B))
+    worst = compare(got, ref, mags, range(B), hq, lens, max_len)
+    assert np.isnan(got[-1, 0, 20:37]).all() and not np.isnan(got[-1, 0, :20]).any()
+    print(f"{dtype} d={d} hq={hq} hk={hk} g={g}: worst |err| / sum|qk| = {worst:.2e}")
+
+
+def test_decode_scores_full_decode_batch_sampled():
+    """The 256-sequence decode batch over the 256 x 32768-slot cache, in the launch
+    the benchmark times; 8 whole sequences (shortest, longest and six others)
+    compared with the oracle."""
+    w = W.WORKLOADS[5]
+    bt = W.make_decode_batch(5)
+    lens = bt["seq_len"]
+    shp = rrp.layer_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.rope_theta)
+    got = run_gpu(shp, bt["q"], bt["codes"], bt["scales"], bt["group"], bt["seq_start"], lens, bt["max_len"])
+    order = np.argsort(lens)
+    seqs = sorted(set([int(order[0]), int(order[-1])] + [int(x) for x in order[np.linspace(1, 254, 6).astype(int)]]))
+    sub = np.array(seqs)
+    oshp = O.shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.rope_theta)
+    ref_sub = O.decode_scores(oshp, bt["q"][sub], bt["codes"], bt["scales"], bt["group"], bt["seq_start"][sub],
+                              lens[sub], bt["max_len"], n_slots=bt["n_slots"])
+    ref = np.full((len(lens), w.n_q_heads, bt["max_len"]), -np.inf)
+    ref[sub] = ref_sub
+    mags = magnitude(bt["q"], bt["codes"], bt["scales"], bt["group"], bt["seq_start"], lens, bt["max_len"],
+                     w.n_q_heads, w.n_kv_heads, seqs)
+    worst = compare(got, ref, mags, seqs, w.n_q_heads, lens, bt["max_len"])
+    written = np.isfinite(got).sum()
+    assert written == int(np.minimum(lens, bt["max_len"]).sum()) * w.n_q_heads
+    print(f"sequences {seqs}: worst |err| / sum|qk| = {worst:.2e}")
+
+
+@pytest.mark.parametrize("b,g", [(128, 64), (2, 64), (128, 128)])
+def test_rotate_then_decode_matches_exact_rope_logits(b, g):
+    """End to end on the GPU: rrp_rotate_quantize_qk writes the cache of a 300-token
+    prefix and the rotated query of the next token; rrp_decode_scores reads them.
+    Every logit stays within the quantisation bound of the exact RoPE logit (the
+    rotation cancels in Q K^T): |err| <= sum_c |q_c| s_h(c) / 2 + bf16 rounding of q."""
+    w = W.WORKLOADS[3]
+    T, d, hq, hk = 300, w.head_dim, w.n_q_heads, w.n_kv_heads
+    inp = W.make_inputs(3, n_tokens=T + 1)
+    rng = np.random.Generator(np.random.PCG64(950 + b))
+    ang = rng.uniform(-math.pi / 4, math.pi / 4, d // 2).astype(np.float32)
+    shp = rrp.layer_shape(hq, hk, d, w.rope_theta)
+    q = to_dev_q(inp["q"][T:T + 1])
+    k = to_dev_q(inp["k"])
+    pos = torch.from_numpy(np.arange(T + 1, dtype=np.int32)).to(DEV)
+    codes, scales = rrp.new_kv4_cache(T + 1, hk, d, g, DEV)
+    rrp.rotate_quantize_qk(shp, None, k, pos, support_b=b, group=g, k_codes=codes, k_scales=scales,
+                           angles=torch.from_numpy(ang).to(DEV))
+    q_out = torch.empty_like(q)
+    c1, s1 = rrp.new_kv4_cache(1, hk, d, g, DEV)
+    rrp.rotate_quantize_qk(shp, q, k[T:T + 1].contiguous(), pos[T:T + 1].contiguous(), support_b=b, group=g,
+                           k_codes=c1, k_scales=s1, angles=torch.from_numpy(ang).to(DEV), q_out=q_out)
+    out = torch.empty((1, hq, T), dtype=torch.float32, device=DEV)
+    rrp.decode_scores(shp, q_out, codes, scales, group=g, seq_start=torch.zeros(1, dtype=torch.int64, device=DEV),
+                      seq_len=torch.full((1,), T, dtype=torch.int32, device=DEV), max_len=T, scores=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[0].astype(np.float64)
+    qr = q_out.float().cpu().numpy()[0].astype(np.float64)
+    s_h = scales.cpu().numpy().astype(np.float64)
+    inv = O.inv_freq(w.rope_theta, d)
+    qv = q_values(inp["q"])
+    kv_ = q_values(inp["k"])
+    worst = 0.0
+    for h in range(hq):
+        kvh = h * hk // hq
+        qe = O.rope_row(qv[T, h], 0, inv, T)
+        nq = float(np.linalg.norm(qe))
+        for j in range(T):
+            ke = O.rope_row(kv_[j, kvh], 0, inv, j)
+            nk = float(np.linalg.norm(ke))
+            exact = float(np.dot(qe, ke))
+            half = np.repeat(s_h[j, kvh], g) / 2
+            quant = float(np.sum(np.abs(qr[h]) * half))                 # K codes: |khat - k| <= s_h / 2
+            qround = 2.0 ** -8 * nq * nk                                   # bf16 query (Cauchy-Schwarz)
+            qcalc = 1e-5 * float(np.max(np.abs(qr[h]))) * math.sqrt(d) * nk  # fp32 transform of q
+            accum = 1e-5 * float(np.linalg.norm(qr[h])) * (nk + float(np.linalg.norm(half)))
+            bound = (quant + qround + qcalc + accum) * (1 + 1e-9)
+            assert abs(got[h, j] - exact) <= bound, (h, j, got[h, j], exact, bound)
+            worst = max(worst, abs(got[h, j] - exact) / bound)
+    print(f"b={b} g={g}: worst |err| / bound = {worst:.3f}")

@@ -202,7 +202,7 @@ int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, 
  * dtype       dtype of q: RRP_BF16 or RRP_F32.
  * q           [n_seqs][n_q_heads][head_dim] rotated queries (the q_out of
  *             rrp_rotate_quantize_qk for the decode tokens), 16-byte aligned.
- * k_codes     uint8 [n_slots][n_kv_heads][head_dim/2], 4-byte aligned.
+ * k_codes     uint8 [n_slots][n_kv_heads][head_dim/2], aligned to head_dim/8 bytes.
  * k_scales    uint16 fp16 bits [n_slots][n_kv_heads][head_dim/group], aligned to
  *             min(2 * head_dim/group, 8) bytes.
  * group       the group size the cache was written with (power of two in [2, head_dim]).

@@ -254,7 +254,7 @@ RRP_EXPORT int rrp_decode_scores(const rrp_shape* shape, int32_t dtype, const vo
         scores == nullptr)
         return RRP_ERR_INVALID_ARG;
     const uintptr_t scale_align = 2 * (d / group) < 8 ? 2 * (d / group) : 8;
-    if (!aligned(q, 16) || !aligned(k_codes, 4) || !aligned(k_scales, scale_align) || !aligned(seq_start, 8) ||
+    if (!aligned(q, 16) || !aligned(k_codes, d / 8) || !aligned(k_scales, scale_align) || !aligned(seq_start, 8) ||
         !aligned(seq_len, 4) || !aligned(scores, 4))
         return RRP_ERR_MISALIGNED;
     rrp::DecodeArgs a{};

@@ -14,10 +14,12 @@
 // per-group partial sums in fp32, so the codes never meet a rounded scale.
 //
 // Lane roles (16x16x32 layout): A row i = lane % 16 (key), k block kb = lane / 16
-// (8 channels); B column j = lane % 16 (query head); D holds keys 4 * (lane / 16)
-// + r, r = 0..3, of column lane % 16.  Inside a lane's 8 channels the element order
-// is (0, 4, 1, 5, 2, 6, 3, 7): that is the order in which the nibble-to-f16
-// conversion produces them, and B is laid out the same way.
+// (8 channels per MFMA); B column j = lane % 16 (query head); D holds keys
+// 4 * (lane / 16) + r, r = 0..3, of column lane % 16.  Which channels an MFMA
+// contracts is a free choice as long as A and B agree (see KBM in the kernel).
+// Inside a lane's 8 channels the element order is (0, 4, 1, 5, 2, 6, 3, 7): that
+// is the order in which the nibble-to-f16 conversion produces them, and B is laid
+// out the same way.
 #include <type_traits>
 
 #include "rrp_device.hpp"
@@ -37,7 +39,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #endif
 constexpr int kKeysPerWave = RRP_DECODE_KEYS_PER_WAVE;
 #ifndef RRP_DECODE_TILES_PER_STEP
-#define RRP_DECODE_TILES_PER_STEP 4
+#define RRP_DECODE_TILES_PER_STEP 2
 #endif
 constexpr int kTilesPerStep = RRP_DECODE_TILES_PER_STEP;  // 16-key tiles loaded per step
 
@@ -108,6 +110,16 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
     constexpr int NG = D / GS;                                  // groups per key row
     constexpr int SPLIT = ElemInfo<E>::bytes == 4 ? 2 : 1;      // f16 terms per query value
     constexpr int SROW = NG * 2;                                // scale bytes per key row
+    // Channel order.  Groups of at least D/4 channels ("kb-major"): lane block kb
+    // owns the contiguous quarter [kb D/4, (kb + 1) D/4) of every row, read with one
+    // 16-byte (D = 128) or 8-byte (D = 64) load per key, and MFMA m takes its m-th
+    // 8-channel piece; a group then covers whole lane blocks, and its partial sum is
+    // separated by masking the query operand to those blocks.  Smaller groups
+    // ("m-major"): MFMA m takes the 32 consecutive channels [32 m, 32 m + 32),
+    // lane block kb the 8 at 32 m + 8 kb.
+    constexpr bool KBM = GS >= D / 4;
+    constexpr int LSPAN = D / 4;                // channels per lane block (kb-major)
+    constexpr int KPG = KBM ? GS / LSPAN : 1;   // lane blocks per group (kb-major)
 
     const int lane = (int)__lane_id();
     const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -134,7 +146,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
     const unsigned char* scales = reinterpret_cast<const unsigned char*>(a.k_scales);
     const size_t code_row = (size_t)D / 2, scale_row = SROW;
     const size_t slot_stride_c = (size_t)hk * code_row, slot_stride_s = (size_t)hk * scale_row;
-    const unsigned char* codes_h = codes + (size_t)kvh * code_row + 4 * kb;
+    const unsigned char* codes_h = codes + (size_t)kvh * code_row + (KBM ? LSPAN / 2 : 4) * kb;
     const unsigned char* scales_h = scales + (size_t)kvh * scale_row;
     // Every key of this wave's chunk sits inside the cache (the usual case):
     // keys are then only clamped to the chunk, with no 64-bit range checks.
@@ -165,9 +177,17 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
         auto load_a = [&](int key0, unsigned (&w)[NM]) {
             bool ok;
             const unsigned char* row = row_of(key0 + col, false, ok);
+            if constexpr (KBM && NM == 4) {
+                const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row));
+                w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            } else if constexpr (KBM) {
+                const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row));
+                w[0] = v.x; w[1] = v.y;
+            } else {
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
-                w[m] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(row + 16 * m));
+                for (int m = 0; m < NM; ++m)
+                    w[m] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(row + 16 * m));
+            }
             if (!FAST || key0 + 16 > k_end) {
 #pragma unroll
                 for (int m = 0; m < NM; ++m) w[m] = ok ? w[m] : 0u;
@@ -206,7 +226,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
         // Groups of at least 32 channels: the key's whole scale row (<= 8 bytes) is
         // loaded with its codes, kept as raw fp16 words until used.  Smaller groups:
         // each MFMA's scales are read when it is used.
-        constexpr int NSW = GS >= 32 ? (SROW + 3) / 4 : 1;
+        constexpr int NSW = KBM ? (SROW + 3) / 4 : 1;
         auto load_sw = [&](int key0, unsigned (&sw)[4][NSW]) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -235,12 +255,13 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
 #pragma unroll
             for (int tt = 0; tt < TP; ++tt) {
                 load_a(s0 + 16 * tt, w[tt]);
-                if constexpr (GS >= 32) load_sw(s0 + 16 * tt, sw[tt]);
+                if constexpr (KBM) load_sw(s0 + 16 * tt, sw[tt]);
             }
         };
         load_step(k_begin, wc, sc);  // the first codes are in flight while the queries are prepared
 
-        // ---- B operand: this lane's query channels 32 m + 8 kb + elem_channel(e) ----
+        // ---- B operand: this lane's query channels (kb-major: LSPAN kb + 8 m + elem_channel(e);
+        //      m-major: 32 m + 8 kb + elem_channel(e)) ----
         float qv[NM][8];
         float qmax = 0.0f;
 #pragma unroll
@@ -249,7 +270,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
             if (head_ok) {
                 const void* row = static_cast<const unsigned char*>(a.q) +
                                   ((size_t)b * a.hq + h) * D * ElemInfo<E>::bytes;
-                QLoad<E>::load(row, 32 * m + 8 * kb, x);
+                QLoad<E>::load(row, KBM ? LSPAN * kb + 8 * m : 32 * m + 8 * kb, x);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = 0.0f;
@@ -275,6 +296,20 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
             }
         float* out_row = a.scores + ((size_t)b * a.hq + h) * a.max_len;
         const float descale = ldexpf(1.0f, -qexp);
+        // kb-major with two groups: the query operand masked to each group's lane blocks
+        constexpr int NGM = (KBM && NG == 2) ? 2 : 1;
+        half8 bqg[NGM][SPLIT][NM];
+        if constexpr (NGM == 2) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int t = 0; t < SPLIT; ++t)
+#pragma unroll
+                    for (int m = 0; m < NM; ++m)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            bqg[q][t][m][e] = (kb / KPG == q) ? bq[t][m][e] : (_Float16)0.0f;
+        }
 
         // One 16-key tile: dequantise, contract on the matrix cores, scale, store.
         auto tile = [&](int key0, const unsigned (&w)[NM], const unsigned (&sw)[4][NSW]) {
@@ -283,16 +318,20 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
             for (int m = 0; m < NM; ++m) am[m] = codes_to_half8(w[m]);
 
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            if constexpr (GS >= 32) {
-                constexpr int MPG = GS / 32;  // MFMAs per group
+            if constexpr (KBM) {
 #pragma unroll
                 for (int gq = 0; gq < NG; ++gq) {
                     f32x4 dq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int m = gq * MPG; m < (gq + 1) * MPG; ++m)
+                    for (int m = 0; m < NM; ++m)
 #pragma unroll
-                        for (int t = 0; t < SPLIT; ++t)
-                            dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(am[m], bq[t][m], dq, 0, 0, 0);
+                        for (int t = 0; t < SPLIT; ++t) {
+                            half8 bm;
+                            if constexpr (NG == 1) bm = bq[t][m];
+                            else if constexpr (NGM == 2) bm = bqg[gq][t][m];
+                            else bm = (kb / KPG == gq) ? bq[t][m] : half8{};
+                            dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(am[m], bm, dq, 0, 0, 0);
+                        }
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float scl = f16_bits_to_f32((unsigned short)(sw[r][gq >> 1] >> (16 * (gq & 1))));

@@ -111,6 +111,7 @@ def test_decode_scores_validation(lib):
     assert dec(q=None) == 1 and dec(codes=None) == 1 and dec(scales=None) == 1
     assert dec(start=None) == 1 and dec(lens=None) == 1 and dec(out=None) == 1
     assert dec(q=P2) == 2 and dec(codes=P2) == 2 and dec(start=ctypes.c_void_p((1 << 20) + 4)) == 2
+    assert dec(codes=ctypes.c_void_p((1 << 20) + 8)) == 2                      # d = 128 rows: 16-byte loads
     assert dec(scales=ctypes.c_void_p((1 << 20) + 2), g=32) == 2   # 8-byte scale rows need 8-byte alignment
     assert dec(shape=_shape(d=96)) == 3
 

@@ -232,12 +232,25 @@ def main():
         stats_bytes = hk * d * 2 * T + 4 * T
         cal_ms = ev[0].elapsed_time(ev[1]) / reps
         st_ms = ev[2].elapsed_time(ev[3]) / reps
+        # Supporting pass 3: the whole support sweep b = 1 .. 128 in one call.
+        sweep = torch.empty((len(rrp.sweep_supports(d)), 8), dtype=torch.float64, device=dev)
+        rrp.quant_error_sweep(shape, k, pos, group=g, stats_out=sweep, angles=angles)
+        ev[2].record(stream)
+        for _ in range(reps):
+            rrp.quant_error_sweep(shape, k, pos, group=g, stats_out=sweep, angles=angles)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        sw_ms = ev[2].elapsed_time(ev[3]) / reps
+        sw = sweep.cpu().numpy()
         supporting.update({"calibrate_angles_ms": cal_ms,
                            "calibrate_angles_hbm_gbs": calib_bytes / (cal_ms * 1e-3) / 1e9,
                            "quant_error_stats_ms": st_ms,
                            "quant_error_stats_hbm_gbs": stats_bytes / (st_ms * 1e-3) / 1e9,
                            "rel_quant_error_b128": float(np.sqrt(st[0] / st[1])),
-                           "mean_k_range_b128": float(st[2] / st[5])})
+                           "mean_k_range_b128": float(st[2] / st[5]),
+                           "quant_error_sweep_ms": sw_ms,
+                           "sweep_rel_quant_error": {str(int(r[7])): float(np.sqrt(r[0] / r[1])) for r in sw},
+                           "sweep_mean_k_range": {str(int(r[7])): float(r[2] / r[5]) for r in sw}})
     torch.cuda.synchronize()
 
     def step():

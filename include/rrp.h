@@ -185,6 +185,23 @@ int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, 
                           int64_t n_tokens, const float* angles, int32_t support_b, int32_t group,
                           double* stats_out, void* stream);
 
+/* rrp_quant_error_sweep -- the support interpolation in one pass ("contributions"
+ * and "results" sections: K range and relative quantisation error as the block
+ * Hadamard support grows from 2 to head_dim).  Reads K twice (one launch per
+ * half of the supports) and writes, for
+ * every support b = 2^j, j = 0 .. log2(head_dim) (b = 1: no Hadamard), the
+ * statistics rrp_quant_error_stats gives at that b (same angles and group):
+ *   stats_out  double[log2(head_dim) + 1][8], row j = { E, N, sum of group max|y|,
+ *              max of group max|y|, sum of group (max y - min y), n_groups,
+ *              n_rows, b }  (overwritten).
+ * Each row matches a separate rrp_quant_error_stats call up to the order of
+ * fp64 rounding (the transform of support 2^j is built from the one of support
+ * 2^(j-1) by one more butterfly stage).  Allocates a stream-ordered scratch
+ * buffer of at most 4096 * 8 * 5 doubles on `stream`.  Errors as
+ * rrp_quant_error_stats. */
+int rrp_quant_error_sweep(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
+                          int64_t n_tokens, const float* angles, int32_t group, double* stats_out, void* stream);
+
 /* rrp_decode_scores -- decode attention logits read straight from the KV4 cache
  * (LLM rotation-quantisation notes, section 3.2.1: the head-wise rotation
  * cancels inside Q K^T, so the rotated query against the rotated key is the

@@ -17,7 +17,8 @@ RRP_ROPE_HALF_SPLIT, RRP_ROPE_INTERLEAVED = 0, 1
 
 # Symbols declared in include/rrp.h.
 EXPORTS = ("rrp_rotate_quantize_qk", "rrp_rotate_quantize_qkv", "rrp_calibrate_angles",
-           "rrp_quant_error_stats", "rrp_decode_scores", "rrp_status_string", "rrp_version")
+           "rrp_quant_error_stats", "rrp_quant_error_sweep", "rrp_decode_scores", "rrp_status_string",
+           "rrp_version")
 
 
 class RrpShape(ctypes.Structure):
@@ -54,10 +55,11 @@ def load():
     L.rrp_rotate_quantize_qkv.argtypes = [sp, i32, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, vp, vp,
                                           i64, vp, vp, vp, vp, vp, vp]
     L.rrp_calibrate_angles.argtypes = [sp, i32, vp, vp, vp, i64, i32, vp, vp, vp]
+    L.rrp_quant_error_sweep.argtypes = [sp, i32, vp, vp, i64, vp, i32, vp, vp]
     L.rrp_decode_scores.argtypes = [sp, i32, vp, i64, vp, vp, i32, i64, vp, vp, i32, vp, vp]
     L.rrp_quant_error_stats.argtypes = [sp, i32, vp, vp, i64, vp, i32, i32, vp, vp]
     for f in ("rrp_rotate_quantize_qk", "rrp_rotate_quantize_qkv", "rrp_calibrate_angles", "rrp_quant_error_stats",
-              "rrp_decode_scores"):
+              "rrp_quant_error_sweep", "rrp_decode_scores"):
         getattr(L, f).restype = ctypes.c_int
     L.rrp_status_string.argtypes = [ctypes.c_int]
     L.rrp_status_string.restype = ctypes.c_char_p

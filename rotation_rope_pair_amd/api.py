@@ -169,6 +169,33 @@ def quant_error_stats(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, su
     _abi.check("rrp_quant_error_stats", L.rrp_quant_error_stats(*args))
 
 
+def sweep_supports(head_dim: int):
+    """The supports b = 1, 2, 4, ..., head_dim covered by quant_error_sweep (row order)."""
+    out, b = [], 1
+    while b <= head_dim:
+        out.append(b)
+        b <<= 1
+    return out
+
+
+def quant_error_sweep(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, group: int, stats_out: torch.Tensor,
+                      angles: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue rrp_quant_error_sweep: the statistics of quant_error_stats for every
+    support b = 1, 2, 4, ..., head_dim into stats_out double[len(supports)][8]
+    (see include/rrp.h)."""
+    L = _abi.load()
+    d, hk = shape.head_dim, shape.n_kv_heads
+    T = int(pos.numel())
+    dt, dev = k.dtype, k.device
+    args = [
+        ctypes.byref(shape), _dtype_code(k), _dev(k, "k", T * hk * d, dt, dev),
+        _dev(pos, "pos", T, torch.int32, dev), T,
+        _dev(angles, "angles", d // 2, torch.float32, dev), int(group),
+        _dev(stats_out, "stats_out", 8 * len(sweep_supports(d)), torch.float64, dev), _stream_ptr(stream, dev),
+    ]
+    _abi.check("rrp_quant_error_sweep", L.rrp_quant_error_sweep(*args))
+
+
 def decode_scores(shape: RrpShape, q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, *, group: int,
                   seq_start: torch.Tensor, seq_len: torch.Tensor, max_len: int, scores: torch.Tensor,
                   n_slots: Optional[int] = None, stream=None) -> None:
@@ -192,6 +219,6 @@ def decode_scores(shape: RrpShape, q: torch.Tensor, k_codes: torch.Tensor, k_sca
     _abi.check("rrp_decode_scores", L.rrp_decode_scores(*args))
 
 
-__all__ = ["layer_shape", "decode_scores", "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
+__all__ = ["layer_shape", "decode_scores", "quant_error_sweep", "sweep_supports", "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
            "new_moments", "RrpError", "RrpShape", "ESTIMATORS", "RRP_F32", "RRP_BF16",
            "RRP_ROPE_HALF_SPLIT", "RRP_ROPE_INTERLEAVED"]

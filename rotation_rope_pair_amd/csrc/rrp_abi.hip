@@ -200,25 +200,33 @@ RRP_EXPORT int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const
     return rrp::launch_calibrate_final(f, s) == hipSuccess ? RRP_OK : RRP_ERR_HIP;
 }
 
-RRP_EXPORT int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
-                                     int64_t n_tokens, const float* angles, int32_t support_b, int32_t group,
-                                     double* stats_out, void* stream) {
+namespace {
+
+// Shared body of the single-support and sweep diagnostics (support_b is ignored
+// by the sweep, which covers b = 1, 2, 4, ..., head_dim).
+int quant_error(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos, int64_t n_tokens,
+                const float* angles, int32_t support_b, int32_t group, bool sweep, double* stats_out, void* stream) {
     int st = check_shape(shape, dtype);
     if (st != RRP_OK) return st;
-    if ((st = check_b_g(shape, support_b, group)) != RRP_OK) return st;
+    if ((st = check_b_g(shape, sweep ? 1 : support_b, group)) != RRP_OK) return st;
     if (n_tokens < 0 || stats_out == nullptr) return RRP_ERR_INVALID_ARG;
     if (n_tokens > 0 && (k == nullptr || pos == nullptr)) return RRP_ERR_INVALID_ARG;
     if (!aligned(k, 16) || !aligned(pos, 4) || !aligned(angles, 4) || !aligned(stats_out, 8))
         return RRP_ERR_MISALIGNED;
     const hipStream_t s = (hipStream_t)stream;
+    int n_sets = 1;
+    if (sweep)
+        for (int b = 1; b < shape->head_dim; b <<= 1) ++n_sets;
     rrp::StatsFinalArgs f{};
     f.stats_out = stats_out;
+    f.n_sets = n_sets;
+    f.sweep = sweep ? 1 : 0;
     f.n_rows = (double)n_tokens * shape->n_kv_heads;
     f.n_groups = f.n_rows * (shape->head_dim / group);
     Scratch scratch;
     if (n_tokens > 0) {
         const int nb = rrp::stats_blocks(n_tokens);
-        if (scratch.alloc((size_t)nb * 5 * sizeof(double), s) != hipSuccess) return RRP_ERR_HIP;
+        if (scratch.alloc((size_t)nb * n_sets * 5 * sizeof(double), s) != hipSuccess) return RRP_ERR_HIP;
         rrp::StatsArgs a{};
         a.k = k;
         a.pos = pos;
@@ -226,15 +234,30 @@ RRP_EXPORT int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, cons
         a.partials = static_cast<double*>(scratch.p);
         a.n_tokens = n_tokens;
         a.hk = shape->n_kv_heads;
-        a.support_b = support_b;
+        a.support_b = sweep ? 1 : support_b;
         a.group = group;
-        a.rsqrt_b = 1.0 / sqrt((double)support_b);
+        a.rsqrt_b = 1.0 / sqrt((double)a.support_b);
         fill_inv_freq(shape, a.inv_freq);
-        if (rrp::launch_stats(a, nb, dtype, shape->head_dim, shape->rope_layout, s) != hipSuccess) return RRP_ERR_HIP;
+        if (rrp::launch_stats(a, nb, dtype, shape->head_dim, shape->rope_layout, sweep, s) != hipSuccess)
+            return RRP_ERR_HIP;
         f.partials = a.partials;
         f.n_blocks = nb;
     }
     return rrp::launch_stats_final(f, s) == hipSuccess ? RRP_OK : RRP_ERR_HIP;
+}
+
+}  // namespace
+
+RRP_EXPORT int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
+                                     int64_t n_tokens, const float* angles, int32_t support_b, int32_t group,
+                                     double* stats_out, void* stream) {
+    return quant_error(shape, dtype, k, pos, n_tokens, angles, support_b, group, false, stats_out, stream);
+}
+
+RRP_EXPORT int rrp_quant_error_sweep(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
+                                     int64_t n_tokens, const float* angles, int32_t group, double* stats_out,
+                                     void* stream) {
+    return quant_error(shape, dtype, k, pos, n_tokens, angles, 1, group, true, stats_out, stream);
 }
 
 RRP_EXPORT int rrp_decode_scores(const rrp_shape* shape, int32_t dtype, const void* q, int64_t n_seqs,

@@ -50,9 +50,11 @@ struct StatsArgs {
 };
 
 struct StatsFinalArgs {
-    const double* partials;
-    double* stats_out;
+    const double* partials;  // [n_sets * 5][n_blocks]
+    double* stats_out;       // [n_sets][8]
     int32_t n_blocks;
+    int32_t n_sets;          // supports reduced (1, or log2(head_dim) + 1 for the sweep)
+    int32_t sweep;           // write the support 2^set into column 7
     double n_groups;
     double n_rows;
 };
@@ -80,7 +82,8 @@ hipError_t launch_calibrate(const CalibArgs& a, int dtype, int head_dim, int lay
 hipError_t launch_calibrate_final(const CalibFinalArgs& a, hipStream_t st);
 
 int stats_blocks(int64_t n_tokens);
-hipError_t launch_stats(const StatsArgs& a, int n_blocks, int dtype, int head_dim, int layout, hipStream_t st);
+hipError_t launch_stats(const StatsArgs& a, int n_blocks, int dtype, int head_dim, int layout, bool sweep,
+                        hipStream_t st);
 hipError_t launch_stats_final(const StatsFinalArgs& a, hipStream_t st);
 
 int64_t decode_chunks(int max_len);

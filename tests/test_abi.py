@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["rrp_calibrate_angles", "rrp_quant_error_stats", "rrp_rotate_quantize_qk",
-                                           "rrp_rotate_quantize_qkv", "rrp_decode_scores", "rrp_status_string",
-                                           "rrp_version"])
+                                           "rrp_rotate_quantize_qkv", "rrp_decode_scores", "rrp_quant_error_sweep",
+                                           "rrp_status_string", "rrp_version"])
 
 
 def test_library_exports_exactly_the_declared_symbols(lib):
@@ -133,6 +133,14 @@ def test_stats_validation(lib):
         return lib.rrp_quant_error_stats(ctypes.byref(_shape()), 1, k, pos, T, None, b, g, out, None)
     assert stt(out=None) == 1 and stt(k=None) == 1 and stt(b=5) == 1 and stt(g=3) == 1
     assert stt(out=ctypes.c_void_p((1 << 20) + 4)) == 2
+
+
+def test_sweep_validation(lib):
+    def swp(T=4, k=P16, pos=P16, g=128, out=P16, shape=None):
+        return lib.rrp_quant_error_sweep(ctypes.byref(shape or _shape()), 1, k, pos, T, None, g, out, None)
+    assert swp(out=None) == 1 and swp(k=None) == 1 and swp(g=3) == 1 and swp(g=256) == 1 and swp(T=-1) == 1
+    assert swp(out=ctypes.c_void_p((1 << 20) + 4)) == 2 and swp(k=P2) == 2
+    assert swp(shape=_shape(d=96)) == 3
 
 
 def test_binding_rejects_host_tensors_before_any_launch():

@@ -482,3 +482,57 @@ def test_quant_error_stats_is_deterministic():
     a = run_stats(w, inp["k"], inp["pos"], None, 128, 128)
     b = run_stats(w, inp["k"], inp["pos"], None, 128, 128)
     assert np.array_equal(a, b)
+
+
+def run_sweep(w, k, pos, angles, g):
+    nb = len(rrp.sweep_supports(w.head_dim))
+    st = torch.empty((nb, 8), dtype=torch.float64, device=DEV)
+    rrp.quant_error_sweep(shape_of(w), to_dev(k), to_dev(pos), group=g, stats_out=st,
+                          angles=None if angles is None else to_dev(angles))
+    torch.cuda.synchronize()
+    return st.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,g,with_angles", [(1, 64, True), (2, 64, True), (2, 64, False), (2, 4, True),
+                                              (3, 128, True), (3, 16, False)])
+def test_quant_error_sweep_every_support_matches_oracle(n, g, with_angles):
+    """One launch for every support b = 1 .. head_dim: each row equals the oracle's
+    diagnostic at that b, and the single-support kernel's, to the stated tolerance."""
+    w = W.WORKLOADS[n]
+    T = min(w.n_tokens, 1024)
+    inp = W.make_inputs(n, n_tokens=T)
+    ang = random_angles(w.n_pairs, 900 + n) if with_angles else None
+    sw = run_sweep(w, inp["k"], inp["pos"], ang, g)
+    supports = rrp.sweep_supports(w.head_dim)
+    assert sw.shape[0] == len(supports)
+    for j, b in enumerate(supports):
+        r = O.quant_error_stats(oshape_of(w), inp["k"], inp["pos"], ang, b, g)
+        one = run_stats(w, inp["k"], inp["pos"], ang, b, g)
+        for ref in (r, one):
+            rel = np.abs(sw[j, :5] - ref[:5]) / np.maximum(np.abs(ref[:5]), 1e-300)
+            assert np.all(rel <= STAT_TOL), (b, sw[j], ref, rel)
+        assert sw[j, 5] == r[5] and sw[j, 6] == r[6] and sw[j, 7] == b
+    print(f"workload {n} g={g}: rel_err by b", [round(float(np.sqrt(x[0] / x[1])), 5) for x in sw])
+
+
+def test_quant_error_sweep_prefill_128k_properties():
+    """The full 131072-token prefill: every sweep row equals the single-support
+    kernel at that b, and N (the energy) is the same at every b (orthogonality)."""
+    w, inp = W.WORKLOADS[4], inputs(4)
+    ang = random_angles(w.n_pairs, 904)
+    k, pos = to_dev(inp["k"]), to_dev(inp["pos"])
+    nb = len(rrp.sweep_supports(w.head_dim))
+    st = torch.empty((nb, 8), dtype=torch.float64, device=DEV)
+    rrp.quant_error_sweep(shape_of(w), k, pos, group=128, stats_out=st, angles=to_dev(ang))
+    torch.cuda.synchronize()
+    sw = st.cpu().numpy()
+    one = torch.empty(8, dtype=torch.float64, device=DEV)
+    for j, b in enumerate(rrp.sweep_supports(w.head_dim)):
+        rrp.quant_error_stats(shape_of(w), k, pos, support_b=b, group=128, stats_out=one, angles=to_dev(ang))
+        torch.cuda.synchronize()
+        ref = one.cpu().numpy()
+        rel = np.abs(sw[j, :5] - ref[:5]) / np.maximum(np.abs(ref[:5]), 1e-300)
+        assert np.all(rel <= STAT_TOL), (b, sw[j], ref, rel)
+        assert abs(sw[j, 1] - sw[0, 1]) <= 1e-11 * sw[0, 1]
+        assert sw[j, 6] == w.n_tokens * w.n_kv_heads and sw[j, 7] == b
+    print("rel_err by b", [round(float(np.sqrt(x[0] / x[1])), 5) for x in sw])

@@ -27,6 +27,8 @@ class Shape(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("rope_layout", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
+        ("angle_heads", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -173,8 +175,14 @@ def max_threads():
     return int(lib().orc_max_threads())
 
 
-def shape(n_q_heads, n_kv_heads, head_dim, rope_theta, rope_layout=HALF_SPLIT):
-    return Shape(int(n_q_heads), int(n_kv_heads), int(head_dim), int(rope_layout), float(rope_theta))
+def shape(n_q_heads, n_kv_heads, head_dim, rope_theta, rope_layout=HALF_SPLIT, angle_heads=0):
+    """angle_heads: 0 / 1 = one angle set shared by all heads; n_kv_heads = one per key head."""
+    return Shape(int(n_q_heads), int(n_kv_heads), int(head_dim), int(rope_layout), float(rope_theta),
+                 int(angle_heads), 0)
+
+
+def angle_groups(shp):
+    return shp.angle_heads if shp.angle_heads > 1 else 1
 
 
 def rotate_quantize_qk(shp, q, k, pos, angles, support_b, group, slot_mapping=None,
@@ -253,7 +261,8 @@ def calibrate_moments(shp, q, k, pos, moments=None):
     ka, dtk = _in(k)
     P = shp.head_dim // 2
     if moments is None:
-        moments = np.zeros((P, 2, 6), np.float64)
+        A = angle_groups(shp)
+        moments = np.zeros((P, 2, 6) if A == 1 else (A, P, 2, 6), np.float64)
     rc = lib().orc_calibrate_moments(ctypes.byref(shp), dtk, _p(qa), _p(ka), _p(_c(pos, np.int32)),
                                      ka.shape[0], _p(moments))
     if rc != 0:
@@ -262,15 +271,17 @@ def calibrate_moments(shp, q, k, pos, moments=None):
 
 
 def angles_from_moments(moments, estimator):
+    """moments [..., P, 2, 6] (one set per leading index) -> phi64, phi32 [..., P], abc [..., P, 3]."""
     moments = _c(moments, np.float64)
-    P = moments.shape[0]
-    phi64 = np.zeros(P, np.float64)
-    phi32 = np.zeros(P, np.float32)
-    abc = np.zeros((P, 3), np.float64)
-    rc = lib().orc_angles_from_moments(_p(moments), P, int(estimator), _p(phi64), _p(phi32), _p(abc))
+    lead = moments.shape[:-2]
+    n = int(np.prod(lead))
+    phi64 = np.zeros(n, np.float64)
+    phi32 = np.zeros(n, np.float32)
+    abc = np.zeros((n, 3), np.float64)
+    rc = lib().orc_angles_from_moments(_p(moments), n, int(estimator), _p(phi64), _p(phi32), _p(abc))
     if rc != 0:
         raise ValueError("oracle angles_from_moments rejected its arguments")
-    return phi64, phi32, abc
+    return phi64.reshape(lead), phi32.reshape(lead), abc.reshape(lead + (3,))
 
 
 def quant_error_stats(shp, k, pos, angles, support_b, group):

@@ -252,7 +252,23 @@ static int check_shape(const orc_shape* s)
     if (s->n_q_heads < 0 || s->n_kv_heads <= 0) return -1;
     if (s->rope_layout != ORC_ROPE_HALF_SPLIT && s->rope_layout != ORC_ROPE_INTERLEAVED) return -1;
     if (!(s->rope_theta > 0.0)) return -1;
+    if (s->angle_heads < 0 || (s->angle_heads > 1 && s->angle_heads != s->n_kv_heads)) return -1;
+    if (s->angle_heads > 1 && s->n_q_heads % s->n_kv_heads) return -1;
     return 0;
+}
+
+/* Number of angle sets, and the set of query head h / key head kh (per-head
+ * parameterisation: every query head shares its key head's set, so the
+ * rotation still cancels in Q K^T). */
+static int angle_groups(const orc_shape* s) { return s->angle_heads > 1 ? s->angle_heads : 1; }
+static int q_angle_group(const orc_shape* s, int h)
+{
+    return s->n_q_heads > 0 ? (int)((int64_t)h * angle_groups(s) / s->n_q_heads) : 0;
+}
+static int k_angle_group(const orc_shape* s, int kh) { return (int)((int64_t)kh * angle_groups(s) / s->n_kv_heads); }
+static const float* angle_set(const float* angles, int group, int head_dim)
+{
+    return angles ? angles + (int64_t)group * (head_dim / 2) : NULL;
 }
 
 int orc_rotate_quantize_qk(const orc_shape* s, int dtype, const void* q, const void* k,
@@ -279,7 +295,8 @@ int orc_rotate_quantize_qk(const orc_shape* s, int dtype, const void* q, const v
             for (int h = 0; h < hq; ++h) {
                 const int64_t row = (t * hq + h) * (int64_t)d;
                 for (int c = 0; c < d; ++c) x[c] = load_elem(q, dtype, row + c);
-                orc_transform_row(x, d, s->rope_layout, inv_freq, p, angles, support_b, y);
+                orc_transform_row(x, d, s->rope_layout, inv_freq, p, angle_set(angles, q_angle_group(s, h), d),
+                                  support_b, y);
                 for (int c = 0; c < d; ++c) {
                     if (q_rot) q_rot[row + c] = y[c];
                     if (q_out) {
@@ -295,7 +312,8 @@ int orc_rotate_quantize_qk(const orc_shape* s, int dtype, const void* q, const v
         for (int h = 0; h < hk; ++h) {
             const int64_t row = (t * hk + h) * (int64_t)d;
             for (int c = 0; c < d; ++c) x[c] = load_elem(k, dtype, row + c);
-            orc_transform_row(x, d, s->rope_layout, inv_freq, p, angles, support_b, y);
+            orc_transform_row(x, d, s->rope_layout, inv_freq, p, angle_set(angles, k_angle_group(s, h), d),
+                              support_b, y);
             if (k_rot)
                 for (int c = 0; c < d; ++c) k_rot[row + c] = y[c];
             for (int j = 0; j < ng; ++j) {
@@ -375,7 +393,8 @@ int orc_calibrate_moments(const orc_shape* s, int dtype, const void* q, const vo
                     int lo, hi;
                     orc_pair_channels(d, s->rope_layout, kk, &lo, &hi);
                     const double u = r[lo], v = r[hi];
-                    double* m = moments + ((int64_t)kk * 2 + stream) * ORC_NMOM;
+                    const int grp = stream == ORC_STREAM_Q ? q_angle_group(s, h) : k_angle_group(s, h);
+                    double* m = moments + (((int64_t)grp * P + kk) * 2 + stream) * ORC_NMOM;
                     m[0] += 1.0;
                     m[1] += u;
                     m[2] += v;
@@ -465,7 +484,8 @@ int orc_quant_error_stats(const orc_shape* s, int dtype, const void* k, const in
         for (int h = 0; h < hk; ++h) {
             const int64_t row = (t * hk + h) * (int64_t)d;
             for (int c = 0; c < d; ++c) x[c] = load_elem(k, dtype, row + c);
-            orc_transform_row(x, d, s->rope_layout, inv_freq, pos[t], angles, support_b, y);
+            orc_transform_row(x, d, s->rope_layout, inv_freq, pos[t], angle_set(angles, k_angle_group(s, h), d),
+                              support_b, y);
             for (int j = 0; j < d / group; ++j) {
                 const double* yg = y + j * group;
                 uint16_t sh;

@@ -84,12 +84,18 @@ void orc_pack_nibbles(const int8_t* q, int n, uint8_t* bytes);
 
 /* ---- the three operations ---- */
 
+/* angle_heads: 0 or 1 = one angle set shared by every head of the layer (the
+ * parameterisation the paper evaluates); n_kv_heads = one set per key head,
+ * query head h using the set of its key head h * Hkv / Hq.  Angle arrays are
+ * [angle groups][d/2], moments [angle groups][d/2][2][6]. */
 typedef struct orc_shape {
     int32_t n_q_heads;
     int32_t n_kv_heads;
     int32_t head_dim;
     int32_t rope_layout;
     double rope_theta;
+    int32_t angle_heads;
+    int32_t reserved;
 } orc_shape;
 
 /* Rotate Q and K rows, quantise K rows into the KV4 cache.
@@ -115,8 +121,9 @@ int orc_quantize_v(const orc_shape* s, int dtype, const void* v, int64_t n_token
                    uint8_t* v_codes, uint16_t* v_scales, const int64_t* slot_mapping, int64_t n_slots,
                    double* v_rot, float* v_scale32);
 
-/* Accumulate post-RoPE pair moments into moments[P][2][6] (n, Su, Sv, Suu, Svv, Suv);
- * q may be NULL (Q stream skipped). */
+/* Accumulate post-RoPE pair moments into moments[angle groups][P][2][6] (n, Su, Sv,
+ * Suu, Svv, Suv); each head adds to its angle group; q may be NULL (Q stream
+ * skipped). */
 int orc_calibrate_moments(const orc_shape* s, int dtype, const void* q, const void* k,
                           const int32_t* pos, int64_t n_tokens, double* moments);
 

@@ -38,6 +38,8 @@ MUTANTS = {
                                   "if (in_cache) v_scales[(t * hk + h) * ng + j] = sh;"),
     "decode_gqa_interleaved": ("const int kv = (int)((int64_t)h * hk / hq);", "const int kv = h % hk;"),
     "decode_one_scale_per_row": ("orc_f16_value(srow[c / group])", "orc_f16_value(srow[0])"),
+    "per_head_query_groups_interleaved": ("return s->n_q_heads > 0 ? (int)((int64_t)h * angle_groups(s) / s->n_q_heads) : 0;",
+                                          "return h % angle_groups(s);"),
 }
 
 

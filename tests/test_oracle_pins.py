@@ -780,3 +780,93 @@ def test_decode_scores_approximate_exact_rope_logits(orc, b, g):
             bound = float(np.sum(np.abs(q_rot[0, h]) * np.repeat(s_h[j, kv], g) / 2))
             bound += 2.0 ** -23 * float(np.dot(np.abs(qe), np.abs(ke))) * 8
             assert abs(sc[0, h, j] - exact) <= bound, (h, j, sc[0, h, j], exact, bound)
+
+
+# --------------------------------------------------------------------------
+# Per-head (non-shared) angles: one set per key head, query heads using their
+# key head's set ([RAQK] optimisation objective: the head-shared set is the
+# parameterisation the paper evaluates; this is the per-head one).
+# --------------------------------------------------------------------------
+
+def _ph_layer(seed, hq=8, hk=2, d=32, T=6):
+    rng = _rng(seed)
+    q = (rng.standard_normal((T, hq, d)) * rng.lognormal(0, 0.8, d)).astype(np.float32)
+    k = (rng.standard_normal((T, hk, d)) * rng.lognormal(0, 0.8, d)).astype(np.float32)
+    pos = rng.integers(0, 300, T).astype(np.int32)
+    ang = rng.uniform(-math.pi / 4, math.pi / 4, (hk, d // 2)).astype(np.float32)
+    return q, k, pos, ang
+
+
+@pytest.mark.parametrize("b", [1, 4, 32])
+def test_per_head_angles_keep_each_query_heads_logits(orc, b):
+    """Query head h against its own key head keeps the RoPE inner product; against
+    a key head of another group it does not (the sets differ)."""
+    hq, hk, d = 8, 2, 32
+    q, k, pos, ang = _ph_layer(70 + b, hq, hk, d)
+    shp = orc.shape(hq, hk, d, 1e4, angle_heads=hk)
+    out = orc.rotate_quantize_qk(shp, q, k, pos, ang, b, d)
+    inv = orc.inv_freq(1e4, d)
+    for t in range(len(pos)):
+        for h in range(hq):
+            qe = orc.rope_row(q[t, h].astype(np.float64), 0, inv, pos[t])
+            for kh in range(hk):
+                ke = orc.rope_row(k[t, kh].astype(np.float64), 0, inv, pos[t])
+                got = float(np.dot(out["q_rot"][t, h], out["k_rot"][t, kh]))
+                ref = float(np.dot(qe, ke))
+                same = kh == h * hk // hq
+                close = abs(got - ref) <= 1e-10 * float(np.linalg.norm(qe) * np.linalg.norm(ke))
+                assert close == same, (t, h, kh, got, ref)
+
+
+def test_per_head_with_identical_sets_is_the_shared_path(orc):
+    hq, hk, d = 8, 4, 32
+    q, k, pos, ang = _ph_layer(71, hq, hk, d)
+    shared = ang[0]
+    a = orc.rotate_quantize_qk(orc.shape(hq, hk, d, 1e4), q, k, pos, shared, 8, 16)
+    b = orc.rotate_quantize_qk(orc.shape(hq, hk, d, 1e4, angle_heads=hk), q, k, pos, np.tile(shared, (hk, 1)), 8, 16)
+    for key in ("q_rot", "k_rot", "k_codes", "k_scales"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_per_head_moments_are_each_groups_shared_moments(orc):
+    """Group g's moments are the shared moments of the layer made of group g's
+    query heads and key head g alone."""
+    hq, hk, d = 8, 2, 32
+    q, k, pos, _ = _ph_layer(72, hq, hk, d)
+    mom = orc.calibrate_moments(orc.shape(hq, hk, d, 1e4, angle_heads=hk), q, k, pos)
+    assert mom.shape == (hk, d // 2, 2, 6)
+    G = hq // hk
+    for g in range(hk):
+        sub = orc.calibrate_moments(orc.shape(G, 1, d, 1e4), q[:, g * G:(g + 1) * G], k[:, g:g + 1], pos)
+        assert np.array_equal(mom[g], sub)
+
+
+@pytest.mark.parametrize("est", [0, 1, 2])
+def test_per_head_angle_attains_each_groups_minimum(orc, est):
+    hq, hk, d = 8, 2, 16
+    q, k, pos, _ = _ph_layer(73 + est, hq, hk, d, T=40)
+    shp = orc.shape(hq, hk, d, 1e4, angle_heads=hk)
+    mom = orc.calibrate_moments(shp, q, k, pos)
+    phi64, _, abc = orc.angles_from_moments(mom, est)
+    assert phi64.shape == (hk, d // 2)
+    for g in range(hk):
+        a, b_, c = abc[g, :, 0], abc[g, :, 1], abc[g, :, 2]
+        ph = phi64[g]
+        va = (a + b_) / 2 + (a - b_) / 2 * np.cos(2 * ph) - c * np.sin(2 * ph)
+        vb = (a + b_) / 2 - (a - b_) / 2 * np.cos(2 * ph) + c * np.sin(2 * ph)
+        assert np.allclose(va, (a + b_) / 2, rtol=1e-12, atol=1e-12 * np.abs(a + b_).max())
+        assert np.allclose(vb, (a + b_) / 2, rtol=1e-12, atol=1e-12 * np.abs(a + b_).max())
+    # groups differ: the per-head sets are not all equal
+    assert not np.allclose(phi64[0], phi64[1])
+
+
+def test_per_head_stats_are_the_sum_of_each_groups_stats(orc):
+    hq, hk, d, g = 8, 2, 32, 16
+    q, k, pos, ang = _ph_layer(76, hq, hk, d, T=12)
+    st = orc.quant_error_stats(orc.shape(hq, hk, d, 1e4, angle_heads=hk), k, pos, ang, 8, g)
+    parts = [orc.quant_error_stats(orc.shape(1, 1, d, 1e4), np.ascontiguousarray(k[:, kh:kh + 1]), pos, ang[kh], 8, g)
+             for kh in range(hk)]
+    tot = np.sum(parts, axis=0)
+    for i in (0, 1, 2, 4, 5, 6):
+        assert abs(st[i] - tot[i]) <= 1e-12 * abs(tot[i])
+    assert st[3] == max(p[3] for p in parts)

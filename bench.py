@@ -136,6 +136,39 @@ def qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b
             "qkv_hbm_gbs": nbytes / (ms * 1e-3) / 1e9, "qkv_tokens_per_s": w.n_tokens / (ms * 1e-3)}
 
 
+def per_head_timing(w, q, k, pos, q_out, codes, scales, dev, stream, b, g, reps=50):
+    """The same prefill with one angle set per key head: per-set calibration, then
+    the rotate launch reading each head's own set."""
+    import torch
+    import rotation_rope_pair_amd as rrp
+    hk, d = w.n_kv_heads, w.head_dim
+    shape = rrp.layer_shape(w.n_q_heads, hk, d, w.rope_theta, angle_heads=hk)
+    moments = rrp.new_moments(d, dev, n_sets=hk)
+    angles = torch.empty((hk, d // 2), dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
+    ev[0].record(stream)
+    for _ in range(10):
+        moments.zero_()
+        rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
+    ev[1].record(stream)
+
+    def launch():
+        rrp.rotate_quantize_qk(shape, q, k, pos, support_b=b, group=g, k_codes=codes, k_scales=scales,
+                               angles=angles, q_out=q_out)
+    for _ in range(10):
+        launch()
+    ev[2].record(stream)
+    for _ in range(reps):
+        launch()
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[2].elapsed_time(ev[3]) / reps
+    nbytes = w.bytes_per_token(group=g, with_slot=False) * w.n_tokens
+    return {"per_head_calibrate_angles_ms": ev[0].elapsed_time(ev[1]) / 10,
+            "per_head_rotate_quantize_ms": ms, "per_head_rotate_hbm_gbs": nbytes / (ms * 1e-3) / 1e9}
+
+
 def decode_scores_timing(dev, stream, reps=20):
     """rrp_decode_scores over the 256-sequence decode batch (Mistral-shaped, 32 / 8
     heads, d 128, g 64) reading its 256 x 32768-slot KV4 cache: time per launch and
@@ -287,6 +320,7 @@ def main():
     if not args.hot_path_only:
         supporting["decode256_rotate_quantize_us"] = decode_latency_us(dev, stream)
         supporting.update(qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b, g))
+        supporting.update(per_head_timing(w, q, k, pos, q_out, codes, scales, dev, stream, b, g))
         supporting.update(decode_scores_timing(dev, stream))
 
     out = {

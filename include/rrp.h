@@ -67,13 +67,26 @@ typedef enum rrp_rope_layout { RRP_ROPE_HALF_SPLIT = 0, RRP_ROPE_INTERLEAVED = 1
 
 /* Shape of one attention layer (host struct).  RoPE frequency of pair k is
  * fp32(rope_theta^(-2k/head_dim)) (rounded once from fp64); the angle at
- * position p is the single fp32 product fp32(p) * freq_k. */
+ * position p is the single fp32 product fp32(p) * freq_k.
+ *
+ * angle_heads chooses the pair-angle parameterisation ("optimisation
+ * objective" section: the paper evaluates one angle per frequency pair shared
+ * by all heads of a layer):
+ *   0 or 1      one set of head_dim/2 angles shared by every head;
+ *   n_kv_heads  one set per key head; query head h uses the set of its key head
+ *               h * n_kv_heads / n_q_heads (so the rotation still cancels in
+ *               Q K^T).  Needs n_q_heads a multiple of n_kv_heads and at most 8
+ *               key heads (RRP_ERR_UNSUPPORTED above).
+ * Every other value is RRP_ERR_INVALID_ARG.  "Angle sets" below means 1 or
+ * n_kv_heads accordingly; angle arrays are float[angle sets][head_dim/2]. */
 typedef struct rrp_shape {
     int32_t n_q_heads;   /* >= 0 */
     int32_t n_kv_heads;  /* >= 1 */
     int32_t head_dim;    /* 64 or 128 */
     int32_t rope_layout; /* rrp_rope_layout */
     double rope_theta;   /* > 0 */
+    int32_t angle_heads; /* 0 / 1 (shared) or n_kv_heads (one set per key head) */
+    int32_t reserved;    /* set to 0 */
 } rrp_shape;
 
 /* rrp_rotate_quantize_qk -- the hot path ("methodology" and "contributions"
@@ -94,7 +107,7 @@ typedef struct rrp_shape {
  * q             [n_tokens][n_q_heads][head_dim] or NULL (no Q rows processed).
  * k             [n_tokens][n_kv_heads][head_dim], required.
  * pos           int32[n_tokens] RoPE positions, each in [0, 2^24).
- * angles        float[head_dim/2] pair angles phi_k (output of
+ * angles        float[angle sets][head_dim/2] pair angles phi_k (output of
  *               rrp_calibrate_angles) or NULL for no pair rotation.
  * support_b     1, 2, 4, ..., head_dim; 1 = no Hadamard (pairwise only).
  * group         quantisation group size: a power of two in [2, head_dim].
@@ -152,15 +165,16 @@ int rrp_rotate_quantize_qkv(const rrp_shape* shape, int32_t dtype, const void* q
  *
  * Accumulates, for every pair k and stream S in {Q, K}, the fp64 sums
  * n, sum u, sum v, sum u^2, sum v^2, sum u*v of the post-RoPE pair (u, v) over
- * all tokens and all heads of S into
- *   moments   double[head_dim/2][2][6]  (stream 0 = Q, 1 = K)
+ * all tokens and all heads of S (per-head sets: all heads of the set's group)
+ * into
+ *   moments   double[angle sets][head_dim/2][2][6]  (stream 0 = Q, 1 = K)
  * which the caller zeroes before the first batch and may keep across batches
  * (it is the resumable calibration state).  Tokens are reduced in a fixed order:
  * repeated calls on the same inputs give bit-identical moments.
  * If angles_out != NULL the angles are then finalised from the accumulated
  * moments with `estimator`: centred covariance [[a, c], [c, b]] of the pair,
  *   phi_k = atan2(a - b, 2c) / 2, wrapped into (-pi/4, pi/4]
- * (0 for a degenerate pair or no samples), written as float[head_dim/2].
+ * (0 for a degenerate pair or no samples), written as float[angle sets][head_dim/2].
  *
  * q may be NULL (Q stream not accumulated); then estimator must be K_ONLY.
  * n_tokens == 0 only finalises (if angles_out != NULL).

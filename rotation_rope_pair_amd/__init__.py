@@ -4,9 +4,9 @@ The compute lives in the HIP library librrp.so (C-ABI: include/rrp.h); this
 package is its torch binding plus the seeded synthetic workloads.
 """
 from .api import (ESTIMATORS, RRP_BF16, RRP_F32, RRP_ROPE_HALF_SPLIT, RRP_ROPE_INTERLEAVED, RrpError,
-                  RrpShape, calibrate_angles, decode_scores, layer_shape, new_kv4_cache, new_moments,
+                  RrpShape, angle_sets, calibrate_angles, decode_scores, layer_shape, new_kv4_cache, new_moments,
                   quant_error_stats, quant_error_sweep, rotate_quantize_qk, rotate_quantize_qkv, sweep_supports)
 
 __all__ = ["ESTIMATORS", "RRP_BF16", "RRP_F32", "RRP_ROPE_HALF_SPLIT", "RRP_ROPE_INTERLEAVED", "RrpError",
-           "RrpShape", "calibrate_angles", "decode_scores", "layer_shape", "new_kv4_cache", "new_moments",
+           "RrpShape", "angle_sets", "calibrate_angles", "decode_scores", "layer_shape", "new_kv4_cache", "new_moments",
            "quant_error_stats", "quant_error_sweep", "rotate_quantize_qk", "rotate_quantize_qkv", "sweep_supports"]

@@ -28,6 +28,8 @@ class RrpShape(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("rope_layout", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
+        ("angle_heads", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

@@ -18,8 +18,16 @@ ESTIMATORS = {"default": RRP_EST_DEFAULT, "k_only": RRP_EST_K_ONLY, "stream_bala
 
 
 def layer_shape(n_q_heads: int, n_kv_heads: int, head_dim: int, rope_theta: float,
-                rope_layout: int = RRP_ROPE_HALF_SPLIT) -> RrpShape:
-    return RrpShape(int(n_q_heads), int(n_kv_heads), int(head_dim), int(rope_layout), float(rope_theta))
+                rope_layout: int = RRP_ROPE_HALF_SPLIT, angle_heads: int = 0) -> RrpShape:
+    """angle_heads: 0 (one angle set shared by all heads) or n_kv_heads (one set
+    per key head, query heads using their key head's set)."""
+    return RrpShape(int(n_q_heads), int(n_kv_heads), int(head_dim), int(rope_layout), float(rope_theta),
+                    int(angle_heads), 0)
+
+
+def angle_sets(shape: RrpShape) -> int:
+    """Angle sets of a layer shape: 1 (shared) or n_kv_heads (per key head)."""
+    return shape.angle_heads if shape.angle_heads > 1 else 1
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -60,9 +68,11 @@ def new_kv4_cache(n_slots: int, n_kv_heads: int, head_dim: int, group: int, devi
     return codes, scales
 
 
-def new_moments(head_dim: int, device="cuda") -> torch.Tensor:
-    """Zeroed calibration state double[head_dim/2][2][6]."""
-    return torch.zeros((head_dim // 2, 2, 6), dtype=torch.float64, device=device)
+def new_moments(head_dim: int, device="cuda", n_sets: int = 1) -> torch.Tensor:
+    """Zeroed calibration state double[head_dim/2][2][6] (double[n_sets][head_dim/2][2][6]
+    for per-key-head angle sets)."""
+    shape = (head_dim // 2, 2, 6) if n_sets == 1 else (n_sets, head_dim // 2, 2, 6)
+    return torch.zeros(shape, dtype=torch.float64, device=device)
 
 
 def _rotate_args(shape, q, k, v, pos, support_b, group, k_codes, k_scales, v_codes, v_scales, angles, q_out,
@@ -82,7 +92,7 @@ def _rotate_args(shape, q, k, v, pos, support_b, group, k_codes, k_scales, v_cod
     if v is not None:
         head.append(_dev(v, "v", T * hk * d, dt, dev))
     mid = [_dev(pos, "pos", T, torch.int32, dev), T,
-           _dev(angles, "angles", d // 2, torch.float32, dev), int(support_b), int(group),
+           _dev(angles, "angles", angle_sets(shape) * (d // 2), torch.float32, dev), int(support_b), int(group),
            _dev(q_out, "q_out", T * hq * d, dt, dev),
            _dev(k_codes, "k_codes", n_slots * hk * (d // 2), torch.uint8, dev),
            _dev(k_scales, "k_scales", n_slots * hk * ng, (torch.float16, torch.int16), dev)]
@@ -146,8 +156,8 @@ def calibrate_angles(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor
         ctypes.byref(shape), _dtype_code(k),
         _dev(q, "q", T * hq * d, dt, dev), _dev(k, "k", T * hk * d, dt, dev),
         _dev(pos, "pos", T, torch.int32, dev), T, est,
-        _dev(moments, "moments", (d // 2) * 12, torch.float64, dev),
-        _dev(angles_out, "angles_out", d // 2, torch.float32, dev),
+        _dev(moments, "moments", angle_sets(shape) * (d // 2) * 12, torch.float64, dev),
+        _dev(angles_out, "angles_out", angle_sets(shape) * (d // 2), torch.float32, dev),
         _stream_ptr(stream, dev),
     ]
     _abi.check("rrp_calibrate_angles", L.rrp_calibrate_angles(*args))
@@ -163,7 +173,7 @@ def quant_error_stats(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, su
     args = [
         ctypes.byref(shape), _dtype_code(k), _dev(k, "k", T * hk * d, dt, dev),
         _dev(pos, "pos", T, torch.int32, dev), T,
-        _dev(angles, "angles", d // 2, torch.float32, dev), int(support_b), int(group),
+        _dev(angles, "angles", angle_sets(shape) * (d // 2), torch.float32, dev), int(support_b), int(group),
         _dev(stats_out, "stats_out", 8, torch.float64, dev), _stream_ptr(stream, dev),
     ]
     _abi.check("rrp_quant_error_stats", L.rrp_quant_error_stats(*args))
@@ -190,7 +200,7 @@ def quant_error_sweep(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, gr
     args = [
         ctypes.byref(shape), _dtype_code(k), _dev(k, "k", T * hk * d, dt, dev),
         _dev(pos, "pos", T, torch.int32, dev), T,
-        _dev(angles, "angles", d // 2, torch.float32, dev), int(group),
+        _dev(angles, "angles", angle_sets(shape) * (d // 2), torch.float32, dev), int(group),
         _dev(stats_out, "stats_out", 8 * len(sweep_supports(d)), torch.float64, dev), _stream_ptr(stream, dev),
     ]
     _abi.check("rrp_quant_error_sweep", L.rrp_quant_error_sweep(*args))
@@ -219,6 +229,6 @@ def decode_scores(shape: RrpShape, q: torch.Tensor, k_codes: torch.Tensor, k_sca
     _abi.check("rrp_decode_scores", L.rrp_decode_scores(*args))
 
 
-__all__ = ["layer_shape", "decode_scores", "quant_error_sweep", "sweep_supports", "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
+__all__ = ["layer_shape", "angle_sets", "decode_scores", "quant_error_sweep", "sweep_supports", "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
            "new_moments", "RrpError", "RrpShape", "ESTIMATORS", "RRP_F32", "RRP_BF16",
            "RRP_ROPE_HALF_SPLIT", "RRP_ROPE_INTERLEAVED"]

@@ -30,8 +30,14 @@ int check_shape(const rrp_shape* s, int32_t dtype) {
     if (!(s->rope_theta > 0.0) || !isfinite(s->rope_theta)) return RRP_ERR_INVALID_ARG;
     if (s->head_dim < 2 || (s->head_dim & 1)) return RRP_ERR_INVALID_ARG;
     if (s->head_dim != 64 && s->head_dim != 128) return RRP_ERR_UNSUPPORTED;
+    if (s->angle_heads < 0 || (s->angle_heads > 1 && s->angle_heads != s->n_kv_heads)) return RRP_ERR_INVALID_ARG;
+    if (s->angle_heads > 1 && s->n_q_heads % s->n_kv_heads != 0) return RRP_ERR_INVALID_ARG;
+    if (s->angle_heads > rrp::kMaxAngleSets) return RRP_ERR_UNSUPPORTED;  // per-set tables held in LDS
     return RRP_OK;
 }
+
+// Angle sets of the layer: 1 (shared by all heads) or n_kv_heads (one per key head).
+int angle_sets(const rrp_shape* s) { return s->angle_heads > 1 ? s->angle_heads : 1; }
 
 int check_b_g(const rrp_shape* s, int32_t support_b, int32_t group) {
     if (!is_pow2(support_b) || support_b > s->head_dim) return RRP_ERR_INVALID_ARG;
@@ -120,6 +126,7 @@ int rotate_quantize(const rrp_shape* shape, int32_t dtype, const void* q, const 
     a.hk = shape->n_kv_heads;
     a.support_b = support_b;
     a.group = group;
+    a.angle_sets = angles != nullptr ? angle_sets(shape) : 1;
     a.rsqrt_b = 1.0 / sqrt((double)support_b);
     a.rsqrt_v = 1.0 / sqrt((double)shape->head_dim);
     fill_inv_freq(shape, a.inv_freq);
@@ -170,12 +177,13 @@ RRP_EXPORT int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const
     f.moments = moments;
     f.angles_out = angles_out;
     f.n_pairs = P;
+    f.n_sets = angle_sets(shape);
     f.estimator = estimator;
     Scratch scratch;
     if (n_tokens > 0) {
         int nbq = 0, nbk = 0;
         const bool with_q = q != nullptr && shape->n_q_heads > 0;
-        const int nb = rrp::calib_blocks(n_tokens, with_q, shape->n_q_heads, shape->n_kv_heads, &nbq, &nbk);
+        const int nb = rrp::calib_blocks(n_tokens, with_q, shape->n_q_heads, shape->n_kv_heads, f.n_sets, &nbq, &nbk);
         if (scratch.alloc((size_t)nb * P * 5 * sizeof(double), s) != hipSuccess) return RRP_ERR_HIP;
         rrp::CalibArgs a{};
         a.q = q;
@@ -187,13 +195,14 @@ RRP_EXPORT int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const
         a.hk = shape->n_kv_heads;
         a.nbq = nbq;
         a.nbk = nbk;
+        a.n_sets = f.n_sets;
         fill_inv_freq(shape, a.inv_freq);
         if (rrp::launch_calibrate(a, dtype, shape->head_dim, shape->rope_layout, s) != hipSuccess) return RRP_ERR_HIP;
         f.partials = a.partials;
         f.nbq = nbq;
         f.nbk = nbk;
-        f.n_rows_q = (double)n_tokens * shape->n_q_heads;
-        f.n_rows_k = (double)n_tokens * shape->n_kv_heads;
+        f.n_rows_q = (double)n_tokens * (shape->n_q_heads / f.n_sets);  // rows per set
+        f.n_rows_k = (double)n_tokens * (shape->n_kv_heads / f.n_sets);
     } else if (angles_out == nullptr) {
         return RRP_OK;
     }
@@ -236,6 +245,7 @@ int quant_error(const rrp_shape* shape, int32_t dtype, const void* k, const int3
         a.hk = shape->n_kv_heads;
         a.support_b = sweep ? 1 : support_b;
         a.group = group;
+        a.angle_sets = angles != nullptr ? angle_sets(shape) : 1;
         a.rsqrt_b = 1.0 / sqrt((double)a.support_b);
         fill_inv_freq(shape, a.inv_freq);
         if (rrp::launch_stats(a, nb, dtype, shape->head_dim, shape->rope_layout, sweep, s) != hipSuccess)

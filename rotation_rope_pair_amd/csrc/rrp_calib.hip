@@ -1,8 +1,9 @@
 // rrp_calib.hip -- calibration pass: fp64 post-RoPE pair moments pooled over
 // heads and tokens, then the closed-form minimax-variance angle per pair.
 //
-// Blocks [0, nbq) accumulate the Q stream, blocks [nbq, nbq + nbk) the K
-// stream.  A row of head_dim channels is held by P/4 lanes, each with four
+// Per angle set (one shared set, or one per key head), blocks [0, nbq) of the
+// set's run accumulate the Q stream of its heads, blocks [nbq, nbq + nbk) the
+// K stream.  A row of head_dim channels is held by P/4 lanes, each with four
 // RoPE pairs (two 8-byte loads for bf16, two 16-byte loads for fp32), so the
 // five fp64 sums per pair stay within a few dozen registers.  Each wave walks
 // tokens with a fixed stride and keeps the next group of row passes in flight
@@ -65,11 +66,18 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
     const int grp = lane / LP;
     double2* tab = tab_all[wave];
 
-    const bool is_k = (int)blockIdx.x >= a.nbq;
-    const int bs = is_k ? (int)blockIdx.x - a.nbq : (int)blockIdx.x;
+    // Blocks come in one run of nbq + nbk per angle set; a set's blocks read only
+    // its heads (all heads when the set is shared).
+    const int per_set = a.nbq + a.nbk;
+    const int set = (int)blockIdx.x / per_set;
+    const int local = (int)blockIdx.x % per_set;
+    const bool is_k = local >= a.nbq;
+    const int bs = is_k ? local - a.nbq : local;
     const int nb = is_k ? a.nbk : a.nbq;
     const unsigned char* src = static_cast<const unsigned char*>(is_k ? a.k : a.q);
-    const int nh = is_k ? a.hk : a.hq;
+    const int nh_all = is_k ? a.hk : a.hq;  // heads per token in the tensor
+    const int nh = nh_all / a.n_sets;       // heads of this set
+    const int h0 = set * nh;
     const int npass = (nh + RP - 1) / RP;
     const int nstep = (npass + MAXP - 1) / MAXP;
     const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
@@ -90,7 +98,7 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
         for (int i = 0; i < MAXP; ++i) {
             const int row = (st * MAXP + i) * RP + grp;
             if (st * MAXP + i < npass && row < nh) {
-                const unsigned char* rp = src + ((size_t)t * nh + row) * ROWB;
+                const unsigned char* rp = src + ((size_t)t * nh_all + h0 + row) * ROWB;
                 raw[i][0] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(rp + off0 * EB));
                 raw[i][1] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(rp + off1 * EB));
             } else {
@@ -180,7 +188,7 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
             for (int q = 0; q < kNSum; ++q) red[wave][(s * kCP + j) * kNSum + q] = acc[j][q];
     }
     __syncthreads();
-    const int nbt = a.nbq + a.nbk;
+    const int nbt = per_set * a.n_sets;
     for (int e = (int)threadIdx.x; e < P * kNSum; e += (int)blockDim.x) {
         double sum = 0.0;
         for (int w = 0; w < nwave; ++w) sum += red[w][e];
@@ -188,37 +196,42 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
     }
 }
 
-// One wave per (stream, pair, sum): lane l adds the partials of blocks l, l + 64,
-// ... in order, then the wave folds its lanes with a fixed xor butterfly (every
-// lane ends with the same value), and lane 0 adds it to the caller's moments.
+// One wave per (set, stream, pair, sum): lane l adds the partials of the set's
+// stream blocks l, l + 64, ... in order, then the wave folds its lanes with a
+// fixed xor butterfly (every lane ends with the same value), and lane 0 adds it
+// to the caller's moments.
 __global__ __launch_bounds__(256) void calib_reduce_kernel(const CalibFinalArgs a) {
     const int P = a.n_pairs;
     const int w = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    if (w >= 2 * P * kNSum) return;  // uniform per wave
+    if (w >= a.n_sets * 2 * P * kNSum) return;  // uniform per wave
     const int lane = (int)__lane_id();
-    const int stream = w / (P * kNSum);
-    const int e = w % (P * kNSum);  // pair * 5 + sum
+    const int set = w / (2 * P * kNSum);
+    const int rem = w % (2 * P * kNSum);
+    const int stream = rem / (P * kNSum);
+    const int e = rem % (P * kNSum);  // pair * 5 + sum
     const int k = e / kNSum, j = e % kNSum;
-    const int b0 = stream ? a.nbq : 0;
+    const int per_set = a.nbq + a.nbk;
+    const int b0 = set * per_set + (stream ? a.nbq : 0);
     const int nb = stream ? a.nbk : a.nbq;
     if (nb == 0) return;  // stream not accumulated by this call
-    const int nbt = a.nbq + a.nbk;
+    const int nbt = per_set * a.n_sets;
     const double* part = a.partials + (size_t)e * nbt + b0;
     double sum = 0.0;
     for (int b = lane; b < nb; b += 64) sum += part[b];
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) sum += shfl_xor_d(sum, m);
     if (lane == 0) {
-        double* mom = a.moments + ((size_t)k * 2 + stream) * 6;
+        double* mom = a.moments + (((size_t)set * P + k) * 2 + stream) * 6;
         mom[1 + j] += sum;
         if (j == 0) mom[0] += stream ? a.n_rows_k : a.n_rows_q;
     }
 }
 
-// One thread per pair: estimator, centred covariance, phi* wrapped to (-pi/4, pi/4].
-__global__ __launch_bounds__(64) void calib_angles_kernel(const CalibFinalArgs a) {
-    const int k = (int)threadIdx.x;
-    if (k >= a.n_pairs) return;
+// One thread per (set, pair): estimator, centred covariance, phi* wrapped to
+// (-pi/4, pi/4].
+__global__ __launch_bounds__(512) void calib_angles_kernel(const CalibFinalArgs a) {
+    const int k = (int)threadIdx.x;  // set * P + pair
+    if (k >= a.n_sets * a.n_pairs) return;
     const double* mq = a.moments + (size_t)k * 12;
     const double* mk = mq + 6;
     const bool use_q = a.estimator != 1 && mq[0] > 0.0;
@@ -259,19 +272,20 @@ __global__ __launch_bounds__(64) void calib_angles_kernel(const CalibFinalArgs a
 
 template <typename E, int D, int LAYOUT>
 hipError_t launch_t(const CalibArgs& a, hipStream_t st) {
-    const int blocks = a.nbq + a.nbk;
+    const int blocks = (a.nbq + a.nbk) * a.n_sets;
     hipLaunchKernelGGL((calib_moments_kernel<E, D, LAYOUT, RRP_CALIB_MAXP>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int* nbq, int* nbk) {
-    // About 8 tokens per wave per stream, at most kMaxCalibBlocks blocks, split
-    // between the streams in proportion to their rows.
+int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int n_sets, int* nbq, int* nbk) {
+    // About 8 tokens per wave per stream, at most kMaxCalibBlocks blocks over all
+    // sets, split between the streams in proportion to their rows.
     int64_t want = (n_tokens * (with_q ? 2 : 1) + 31) / 32;
-    if (want < (with_q ? 2 : 1)) want = with_q ? 2 : 1;
     if (want > kMaxCalibBlocks) want = kMaxCalibBlocks;
+    want = (want + n_sets - 1) / n_sets;  // per set
+    if (want < (with_q ? 2 : 1)) want = with_q ? 2 : 1;
     const int total = (int)want;
     if (!with_q || hq == 0) {
         *nbq = 0;
@@ -283,7 +297,7 @@ int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int* nbq, int* n
         *nbq = q;
         *nbk = total - q;
     }
-    return *nbq + *nbk;
+    return (*nbq + *nbk) * n_sets;
 }
 
 hipError_t launch_calibrate(const CalibArgs& a, int dtype, int head_dim, int layout, hipStream_t st) {
@@ -302,13 +316,14 @@ hipError_t launch_calibrate(const CalibArgs& a, int dtype, int head_dim, int lay
 
 hipError_t launch_calibrate_final(const CalibFinalArgs& a, hipStream_t st) {
     if (a.nbq + a.nbk > 0) {
-        const int waves = 2 * a.n_pairs * kNSum;
+        const int waves = a.n_sets * 2 * a.n_pairs * kNSum;
         hipLaunchKernelGGL(calib_reduce_kernel, dim3((waves + 3) / 4), dim3(256), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (a.angles_out == nullptr) return hipSuccess;
-    hipLaunchKernelGGL(calib_angles_kernel, dim3(1), dim3(64), 0, st, a);
+    const int threads = ((a.n_sets * a.n_pairs + 63) / 64) * 64;
+    hipLaunchKernelGGL(calib_angles_kernel, dim3(1), dim3(threads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -244,6 +244,41 @@ __device__ __forceinline__ void token_tables(float2* tab32, double2* tab64, int 
     wave_lds_sync();
 }
 
+// ---------------------------------------------------------------------------
+// Per-head angle sets: one set of pair angles per key head (query heads use
+// their key head's set).  The block keeps cos / sin of every set's angles in
+// LDS (phi[set * P + k]); each token's tables are built for every set:
+// tab64[set * P + k], tab32[set * P + k] (tab32 may be null).
+// ---------------------------------------------------------------------------
+// cos / sin of angles[0 .. n) into phi (block-wide; ends with a block barrier).
+__device__ __forceinline__ void load_angle_sets(double2* phi, const float* angles, int n) {
+    for (int e = (int)threadIdx.x; e < n; e += (int)blockDim.x) {
+        double sv = 0.0, cv = 1.0;
+        if (angles != nullptr) sincos_f64_of_f32(angles[e], sv, cv);
+        phi[e] = make_double2(cv, sv);
+    }
+    __syncthreads();
+}
+
+template <int D, bool FOLD>
+__device__ __forceinline__ void token_tables_sets(float2* tab32, double2* tab64, int lane, int p, float invf,
+                                                  const double2* phi, int n_sets, double rs) {
+    constexpr int P = D / 2;
+    wave_lds_sync();  // the previous token's table reads are complete
+    if (lane < P) {
+        double sa, ca;
+        sincos_f64_of_f32(rope_angle_f32(p, invf), sa, ca);
+        for (int g = 0; g < n_sets; ++g) {
+            const double2 cs = phi[g * P + lane];
+            const double C = (ca * cs.x - sa * cs.y) * rs, S = (sa * cs.x + ca * cs.y) * rs;
+            const double e0 = FOLD ? C + S : C, e1 = FOLD ? C - S : S;
+            tab64[g * P + lane] = make_double2(e0, e1);
+            if (tab32 != nullptr) tab32[g * P + lane] = make_float2((float)e0, (float)e1);
+        }
+    }
+    wave_lds_sync();
+}
+
 // Pair index of each coefficient slot of a lane holding the data of row
 // position s_src:
 //   half-split: slot j = pair s_src*CE + j (chunks 0 / 1 hold its two channels)

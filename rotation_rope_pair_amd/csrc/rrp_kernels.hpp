@@ -19,20 +19,22 @@ struct CalibArgs {
     int64_t n_tokens;
     int32_t hq;
     int32_t hk;
-    int32_t nbq;  // blocks accumulating the Q stream (first nbq blocks)
-    int32_t nbk;  // blocks accumulating the K stream
+    int32_t nbq;     // blocks per angle set accumulating the Q stream
+    int32_t nbk;     // blocks per angle set accumulating the K stream
+    int32_t n_sets;  // angle sets (1: all heads pooled; n_kv_heads: per key head)
     float inv_freq[kMaxPairs];
 };
 
 struct CalibFinalArgs {
     const double* partials;
-    double* moments;  // [P][2][6]
-    float* angles_out;
-    double n_rows_q;  // rows added to the Q stream by this call
+    double* moments;  // [n_sets][P][2][6]
+    float* angles_out;  // [n_sets][P]
+    double n_rows_q;  // rows added to each set's Q stream by this call
     double n_rows_k;
-    int32_t nbq;
+    int32_t nbq;      // blocks per set (as in CalibArgs)
     int32_t nbk;
-    int32_t n_pairs;
+    int32_t n_pairs;  // P
+    int32_t n_sets;
     int32_t estimator;
 };
 
@@ -45,6 +47,7 @@ struct StatsArgs {
     int32_t hk;
     int32_t support_b;
     int32_t group;
+    int32_t angle_sets;  // 1: shared angle set; n_kv_heads: one per key head
     double rsqrt_b;
     float inv_freq[kMaxPairs];
 };
@@ -77,7 +80,7 @@ struct DecodeArgs {
 };
 
 
-int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int* nbq, int* nbk);
+int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int n_sets, int* nbq, int* nbk);
 hipError_t launch_calibrate(const CalibArgs& a, int dtype, int head_dim, int layout, hipStream_t st);
 hipError_t launch_calibrate_final(const CalibFinalArgs& a, hipStream_t st);
 

@@ -108,7 +108,10 @@ template <int R> struct Depth {
 // BT: compile-time Hadamard support (BT == D, the full-head case) or 0 (runtime b).
 // HAS_V: also turn the V rows by the full-head Hadamard and quantise them into
 // the V half of the cache (no RoPE, no pair rotation).
-template <typename E, int D, int LAYOUT, bool SMALLG, int BT, bool HAS_V>
+// PH: one angle set per key head (a.angle_sets of them); query head h uses set
+// h * sets / Hq, key head kh set kh * sets / Hkv.  Blocks then hold at most two
+// waves, so the per-set tables stay within 32 KB of LDS per block.
+template <typename E, int D, int LAYOUT, bool SMALLG, int BT, bool HAS_V, bool PH>
 __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a) {
     using G = Geo<E, D>;
     using LM = LaneMap<G::L>;
@@ -117,8 +120,11 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
     constexpr int ROWB = D * EB;
     constexpr int MQ = Depth<R>::Q, MK = Depth<R>::K;
     constexpr bool FOLD = (LAYOUT == 0) && (BT == D);
-    __shared__ float2 tab32_all[4][P];
-    __shared__ double2 tab64_all[4][P];
+    constexpr int WMAX = PH ? 2 : 4;             // waves per block
+    constexpr int NA = PH ? kMaxAngleSets : 1;   // angle sets held per token
+    __shared__ float2 tab32_all[WMAX][NA * P];
+    __shared__ double2 tab64_all[WMAX][NA * P];
+    __shared__ double2 phi_all[PH ? NA * P : 1];
 
     const int lane = (int)__lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -129,7 +135,8 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
     double2* tab64 = tab64_all[wave];
 
     double cphi = 1.0, sphi = 0.0;
-    if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
+    if constexpr (PH) load_angle_sets(phi_all, a.angles, a.angle_sets * P);
+    else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
     const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
     // Rows are loaded permuted (lane s holds position s ^ perm), see fwht_row.
     const int s_src = s ^ lane_perm_mask<D, CE>(BT ? BT : a.support_b);
@@ -170,7 +177,8 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
                 if (i < nk && i * R + grp < hk) load_row_chunks<E, D>(vt + i * R * ROWB + ld_off, s_src_v, rv[i]);
         }
 
-        token_tables<D, FOLD>(tab32, tab64, lane, p, invf, cphi, sphi, a.rsqrt_b);
+        if constexpr (PH) token_tables_sets<D, FOLD>(tab32, tab64, lane, p, invf, phi_all, a.angle_sets, a.rsqrt_b);
+        else token_tables<D, FOLD>(tab32, tab64, lane, p, invf, cphi, sphi, a.rsqrt_b);
 
         // ---- Q rows (fp32) ----
         for (int c0 = 0; c0 < nq; c0 += MQ) {
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
                 float x[2][CE];
                 unpack_chunk<E, CE>(rq[i][0], x[0]);
                 unpack_chunk<E, CE>(rq[i][1], x[1]);
-                rotate_lds<LAYOUT, FOLD>(x, tab32, kidx);
+                rotate_lds<LAYOUT, FOLD>(x, PH ? tab32 + (h * a.angle_sets / a.hq) * P : tab32, kidx);
                 fwht_row<D, CE, BT, FOLD>(x, a.support_b, s);
                 if (qo) {
 #pragma unroll
@@ -230,8 +238,9 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
                 for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                     for (int i2 = 0; i2 < CE; ++i2) x[ch][i2] = (KV)xf[ch][i2];
-                if constexpr (RRP_K_FP64) rotate_lds<LAYOUT, FOLD>(x, tab64, kidx);
-                else rotate_lds<LAYOUT, FOLD>(x, tab32, kidx);
+                const int kset = PH ? (h * a.angle_sets / hk) * P : 0;
+                if constexpr (RRP_K_FP64) rotate_lds<LAYOUT, FOLD>(x, tab64 + kset, kidx);
+                else rotate_lds<LAYOUT, FOLD>(x, tab32 + kset, kidx);
                 fwht_row<D, CE, BT, FOLD>(x, a.support_b, s);
                 const size_t trow = (size_t)t * hk + h;
                 if (a.k_dbg) {
@@ -297,7 +306,8 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
 template <typename E, int D, int LAYOUT>
 hipError_t launch_t(const RotateArgs& a, hipStream_t st) {
     // Small batches (decode): one wave per block so the tokens spread over all CUs.
-    const int wpb = a.n_tokens >= 4096 ? 4 : 1;
+    const bool ph = a.angle_sets > 1;
+    const int wpb = a.n_tokens >= 4096 ? (ph ? 2 : 4) : 1;
     int64_t blocks = (a.n_tokens + wpb - 1) / wpb;
 #ifndef RRP_MAX_BLOCKS
 #define RRP_MAX_BLOCKS 8192
@@ -305,16 +315,19 @@ hipError_t launch_t(const RotateArgs& a, hipStream_t st) {
     if (blocks > RRP_MAX_BLOCKS) blocks = RRP_MAX_BLOCKS;  // waves then walk several tokens each
     const bool smallg = a.group < Geo<E, D>::CE;
     const dim3 grid((unsigned)blocks), block(64 * wpb);
-#define RRP_LAUNCH(SG, BT, HV) \
-    hipLaunchKernelGGL((rotate_quantize_kernel<E, D, LAYOUT, SG, BT, HV>), grid, block, 0, st, a)
-#define RRP_LAUNCH_B(SG, HV)           \
-    if (a.support_b == D) RRP_LAUNCH(SG, D, HV); \
-    else RRP_LAUNCH(SG, 0, HV)
+#define RRP_LAUNCH(SG, BT, HV, PHV) \
+    hipLaunchKernelGGL((rotate_quantize_kernel<E, D, LAYOUT, SG, BT, HV, PHV>), grid, block, 0, st, a)
+#define RRP_LAUNCH_B(SG, HV, PHV)                   \
+    if (a.support_b == D) RRP_LAUNCH(SG, D, HV, PHV); \
+    else RRP_LAUNCH(SG, 0, HV, PHV)
+#define RRP_LAUNCH_P(SG, HV)                        \
+    if (ph) { RRP_LAUNCH_B(SG, HV, true); } else { RRP_LAUNCH_B(SG, HV, false); }
     if (a.v != nullptr) {
-        if (smallg) { RRP_LAUNCH_B(true, true); } else { RRP_LAUNCH_B(false, true); }
+        if (smallg) { RRP_LAUNCH_P(true, true); } else { RRP_LAUNCH_P(false, true); }
     } else {
-        if (smallg) { RRP_LAUNCH_B(true, false); } else { RRP_LAUNCH_B(false, false); }
+        if (smallg) { RRP_LAUNCH_P(true, false); } else { RRP_LAUNCH_P(false, false); }
     }
+#undef RRP_LAUNCH_P
 #undef RRP_LAUNCH_B
 #undef RRP_LAUNCH
     return hipGetLastError();

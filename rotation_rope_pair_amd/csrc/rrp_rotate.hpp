@@ -7,7 +7,8 @@
 
 namespace rrp {
 
-constexpr int kMaxPairs = 64;  // head_dim <= 128
+constexpr int kMaxPairs = 64;     // head_dim <= 128
+constexpr int kMaxAngleSets = 8;  // per-head angle sets held in LDS per token
 
 // RoPE frequencies travel in the kernel argument block: every lane reads its
 // own pair's entry, so no device table has to be allocated or kept.
@@ -35,6 +36,7 @@ struct RotateArgs {
     int32_t hk;
     int32_t support_b;
     int32_t group;
+    int32_t angle_sets;  // 1: one set shared by all heads; n_kv_heads: one per key head
     double rsqrt_b;
     double rsqrt_v;  // 1 / sqrt(head_dim)
     float inv_freq[kMaxPairs];

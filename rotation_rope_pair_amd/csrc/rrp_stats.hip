@@ -124,7 +124,9 @@ __device__ __forceinline__ void block_stats_partials(StatAcc acc, int set, doubl
     }
 }
 
-template <typename E, int D, int LAYOUT, int BT, bool SMALLG>
+// PH: one angle set per key head (a.angle_sets of them), key head kh using set
+// kh * sets / Hkv; the fp64 tables of every set are kept per wave.
+template <typename E, int D, int LAYOUT, int BT, bool SMALLG, bool PH>
 __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     using G = Geo<E, D>;
     using LM = LaneMap<G::L>;
@@ -132,8 +134,10 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr size_t ROWB = (size_t)D * EB;
     constexpr bool FOLD = (LAYOUT == 0) && (BT == D);
-    __shared__ float2 tab32_all[4][P];
-    __shared__ double2 tab64_all[4][P];
+    constexpr int NA = PH ? kMaxAngleSets : 1;  // angle sets held per token
+    __shared__ float2 tab32_all[4][PH ? 1 : P];  // fp32 tables (unused by per-set tables)
+    __shared__ double2 tab64_all[4][NA * P];
+    __shared__ double2 phi_all[PH ? NA * P : 1];
     __shared__ double red[4][kNStat];
 
     const int lane = (int)__lane_id();
@@ -145,7 +149,8 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     double2* tab64 = tab64_all[wave];
 
     double cphi = 1.0, sphi = 0.0;
-    if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
+    if constexpr (PH) load_angle_sets(phi_all, a.angles, a.angle_sets * P);
+    else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
     const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
     const int s_src = s ^ lane_perm_mask<D, CE>(BT ? BT : a.support_b);  // permuted loads, see fwht_row
     int kidx[CE];
@@ -181,7 +186,10 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
             pn = 0;
         }
         if (tn < a.n_tokens) load_pass(tn, pn, nxt);
-        if (ps == 0) token_tables<D, FOLD>(tab32, tab64, lane, a.pos[t], invf, cphi, sphi, a.rsqrt_b);
+        if (ps == 0) {
+            if constexpr (PH) token_tables_sets<D, FOLD>(nullptr, tab64, lane, a.pos[t], invf, phi_all, a.angle_sets, a.rsqrt_b);
+            else token_tables<D, FOLD>(tab32, tab64, lane, a.pos[t], invf, cphi, sphi, a.rsqrt_b);
+        }
         if (ps * R + grp < a.hk) {
             float yf[2][CE];
             unpack_chunk<E, CE>(cur[0], yf[0]);
@@ -191,7 +199,7 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int i2 = 0; i2 < CE; ++i2) y[ch][i2] = (double)yf[ch][i2];
-            rotate_lds<LAYOUT, FOLD>(y, tab64, kidx);
+            rotate_lds<LAYOUT, FOLD>(y, PH ? tab64 + ((ps * R + grp) * a.angle_sets / a.hk) * P : tab64, kidx);
             fwht_row<D, CE, BT, FOLD>(y, a.support_b, s);
             add_row_stats<D, CE, SMALLG>(y, g, s, acc);
         }
@@ -271,7 +279,7 @@ template <> struct Log2<128> { static constexpr int value = 7; };
 
 // Supports 2^J0 .. 2^(J1-1) of the sweep (the sweep runs as two launches, so
 // each keeps half the per-support sums in registers).
-template <typename E, int D, int LAYOUT, bool SMALLG, int J0, int J1>
+template <typename E, int D, int LAYOUT, bool SMALLG, int J0, int J1, bool PH>
 __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
     using G = Geo<E, D>;
     using LM = LaneMap<G::L>;
@@ -279,8 +287,10 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr size_t ROWB = (size_t)D * EB;
     constexpr int NJ = J1 - J0;
-    __shared__ float2 tab32_all[4][P];
-    __shared__ double2 tab64_all[4][P];
+    constexpr int NA = PH ? kMaxAngleSets : 1;  // angle sets held per token
+    __shared__ float2 tab32_all[4][PH ? 1 : P];  // fp32 tables (unused by per-set tables)
+    __shared__ double2 tab64_all[4][NA * P];
+    __shared__ double2 phi_all[PH ? NA * P : 1];
     __shared__ double red[4][kNStat];
 
     const int lane = (int)__lane_id();
@@ -292,7 +302,8 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
     double2* tab64 = tab64_all[wave];
 
     double cphi = 1.0, sphi = 0.0;
-    if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
+    if constexpr (PH) load_angle_sets(phi_all, a.angles, a.angle_sets * P);
+    else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
     const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
     int kidx[CE];
     pair_index_of_lane<D, LAYOUT, CE>(s, kidx);  // natural chunk order
@@ -326,7 +337,10 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
             pn = 0;
         }
         if (tn < a.n_tokens) load_pass(tn, pn, nxt);
-        if (ps == 0) token_tables<D, false>(tab32, tab64, lane, a.pos[t], invf, cphi, sphi, 1.0);
+        if (ps == 0) {
+            if constexpr (PH) token_tables_sets<D, false>(nullptr, tab64, lane, a.pos[t], invf, phi_all, a.angle_sets, 1.0);
+            else token_tables<D, false>(tab32, tab64, lane, a.pos[t], invf, cphi, sphi, 1.0);
+        }
         if (ps * R + grp < a.hk) {
             float yf[2][CE];
             unpack_chunk<E, CE>(cur[0], yf[0]);
@@ -336,7 +350,7 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int i2 = 0; i2 < CE; ++i2) y[ch][i2] = (double)yf[ch][i2];
-            rotate_lds<LAYOUT, false>(y, tab64, kidx);
+            rotate_lds<LAYOUT, false>(y, PH ? tab64 + ((ps * R + grp) * a.angle_sets / a.hk) * P : tab64, kidx);
             SweepRest<D, CE, SMALLG, 0, J0, J1>::run(y, g, s, acc);
         }
         cur[0] = nxt[0];
@@ -374,23 +388,23 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const StatsFinalArgs a
     }
 }
 
-template <typename E, int D, int LAYOUT>
-hipError_t launch_t(const StatsArgs& a, int n_blocks, bool sweep, hipStream_t st) {
+template <typename E, int D, int LAYOUT, bool PH>
+hipError_t launch_p(const StatsArgs& a, int n_blocks, bool sweep, hipStream_t st) {
     constexpr int CE = Geo<E, D>::CE;
     const bool small = a.group < CE;
     if (sweep) {
         constexpr int NB = Log2<D>::value + 1, JH = NB / 2;
         if (small) {
-            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, true, 0, JH>), dim3(n_blocks), dim3(256), 0, st, a);
-            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, true, JH, NB>), dim3(n_blocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, true, 0, JH, PH>), dim3(n_blocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, true, JH, NB, PH>), dim3(n_blocks), dim3(256), 0, st, a);
         } else {
-            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, false, 0, JH>), dim3(n_blocks), dim3(256), 0, st, a);
-            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, false, JH, NB>), dim3(n_blocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, false, 0, JH, PH>), dim3(n_blocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, false, JH, NB, PH>), dim3(n_blocks), dim3(256), 0, st, a);
         }
         return hipGetLastError();
     }
 #define RRP_LAUNCH(BT, SG) \
-    hipLaunchKernelGGL((stats_kernel<E, D, LAYOUT, BT, SG>), dim3(n_blocks), dim3(256), 0, st, a)
+    hipLaunchKernelGGL((stats_kernel<E, D, LAYOUT, BT, SG, PH>), dim3(n_blocks), dim3(256), 0, st, a)
     if (a.support_b == D) {
         if (small) RRP_LAUNCH(D, true); else RRP_LAUNCH(D, false);
     } else {
@@ -398,6 +412,12 @@ hipError_t launch_t(const StatsArgs& a, int n_blocks, bool sweep, hipStream_t st
     }
 #undef RRP_LAUNCH
     return hipGetLastError();
+}
+
+template <typename E, int D, int LAYOUT>
+hipError_t launch_t(const StatsArgs& a, int n_blocks, bool sweep, hipStream_t st) {
+    if (a.angle_sets > 1) return launch_p<E, D, LAYOUT, true>(a, n_blocks, sweep, st);
+    return launch_p<E, D, LAYOUT, false>(a, n_blocks, sweep, st);
 }
 
 }  // namespace

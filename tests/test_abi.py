@@ -49,9 +49,9 @@ def test_version_and_status_strings(lib):
     assert lib.rrp_status_string(99) == b"unknown status"
 
 
-def _shape(hq=32, hk=8, d=128, layout=0, theta=5e5):
+def _shape(hq=32, hk=8, d=128, layout=0, theta=5e5, ah=0):
     from rotation_rope_pair_amd._abi import RrpShape
-    return RrpShape(hq, hk, d, layout, theta)
+    return RrpShape(hq, hk, d, layout, theta, ah, 0)
 
 
 P16 = ctypes.c_void_p(1 << 20)       # a 16-byte aligned, never dereferenced address
@@ -85,6 +85,21 @@ def test_rotate_validation(lib):
     assert rot(lib, k=P2) == 2 and rot(lib, q=P2, q_out=P16) == 2
     assert rot(lib, codes=P2) == 2 and rot(lib, kd=P2) == 2
     assert rot(lib, slots=ctypes.c_void_p((1 << 20) + 4)) == 2
+
+
+def test_angle_heads_validation(lib):
+    """angle_heads is 0 or 1 (one shared set) or n_kv_heads (one set per key head)."""
+    assert rot(lib, shape=_shape(ah=-1)) == 1
+    assert rot(lib, shape=_shape(ah=4)) == 1                      # neither shared nor n_kv_heads
+    assert rot(lib, shape=_shape(hq=12, hk=8, ah=8)) == 1         # query heads must split evenly
+    assert rot(lib, shape=_shape(hq=32, hk=16, ah=16)) == 3       # more sets than the LDS tables hold
+    assert lib.rrp_calibrate_angles(ctypes.byref(_shape(ah=3)), 1, P16, P16, P16, 4, 0, P16, None, None) == 1
+    assert lib.rrp_quant_error_stats(ctypes.byref(_shape(ah=2)), 1, P16, P16, 4, None, 128, 128, P16,
+                                     None) == 1
+    from rotation_rope_pair_amd import api
+    assert api.angle_sets(api.layer_shape(32, 8, 128, 5e5)) == 1
+    assert api.angle_sets(api.layer_shape(32, 8, 128, 5e5, angle_heads=1)) == 1
+    assert api.angle_sets(api.layer_shape(32, 8, 128, 5e5, angle_heads=8)) == 8
 
 
 def test_rotate_qkv_validation(lib):

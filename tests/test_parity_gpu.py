@@ -44,12 +44,13 @@ def bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def shape_of(w, layout=0):
-    return rrp.layer_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.rope_theta, layout)
+def shape_of(w, layout=0, ah=0):
+    return rrp.layer_shape(w.n_q_heads, w.n_kv_heads, w.head_dim, w.rope_theta, layout, angle_heads=ah)
 
 
-def oshape_of(w, layout=0, hq=None):
-    return O.shape(w.n_q_heads if hq is None else hq, w.n_kv_heads, w.head_dim, w.rope_theta, layout)
+def oshape_of(w, layout=0, hq=None, ah=0):
+    return O.shape(w.n_q_heads if hq is None else hq, w.n_kv_heads, w.head_dim, w.rope_theta, layout,
+                   angle_heads=ah)
 
 
 def random_angles(P, seed):
@@ -68,7 +69,7 @@ def sample_tokens(T, n, seed=0):
 
 
 def run_rotate(w, inp, angles, b, g, *, debug=True, in_place=False, with_q=True, layout=0,
-               q_dev=None, k_dev=None, pos_dev=None):
+               q_dev=None, k_dev=None, pos_dev=None, ah=0):
     d, hq, hk = w.head_dim, w.n_q_heads, w.n_kv_heads
     q = q_dev if q_dev is not None else (to_dev(inp["q"]) if with_q else None)
     k = k_dev if k_dev is not None else to_dev(inp["k"])
@@ -84,19 +85,19 @@ def run_rotate(w, inp, angles, b, g, *, debug=True, in_place=False, with_q=True,
         dbg["k_rot_f32"] = torch.empty((T, hk, d), dtype=torch.float32, device=DEV)
         dbg["k_scale_f32"] = torch.empty((T, hk, d // g), dtype=torch.float32, device=DEV)
     sm = to_dev(inp.get("slot_mapping"))
-    rrp.rotate_quantize_qk(shape_of(w, layout), q, k, pos, support_b=b, group=g, k_codes=codes, k_scales=scales,
+    rrp.rotate_quantize_qk(shape_of(w, layout, ah), q, k, pos, support_b=b, group=g, k_codes=codes, k_scales=scales,
                            angles=None if angles is None else to_dev(angles), q_out=q_out, slot_mapping=sm,
                            n_slots=n_slots, **dbg)
     torch.cuda.synchronize()
     return {"q_out": q_out, "codes": codes, "scales": scales, **dbg}
 
 
-def check_rotate(w, inp, out, angles, b, g, idx, *, layout=0, with_q=True):
+def check_rotate(w, inp, out, angles, b, g, idx, *, layout=0, with_q=True, ah=0):
     """Compare GPU outputs of the tokens `idx` with the oracle run on just those tokens."""
     d, hq, hk = w.head_dim, w.n_q_heads, w.n_kv_heads
     idx = np.asarray(idx)
     q = inp["q"][idx] if with_q else None
-    ref = O.rotate_quantize_qk(oshape_of(w, layout, hq if with_q else 0), q, inp["k"][idx], inp["pos"][idx],
+    ref = O.rotate_quantize_qk(oshape_of(w, layout, hq if with_q else 0, ah), q, inp["k"][idx], inp["pos"][idx],
                                angles, b, g)
     sm = inp.get("slot_mapping")
     slots = idx if sm is None else sm[idx]
@@ -300,7 +301,7 @@ def vinputs(n, T=None):
     return _VINPUTS[key]
 
 
-def run_rotate_qkv(w, inp, angles, b, g, *, debug=True):
+def run_rotate_qkv(w, inp, angles, b, g, *, debug=True, ah=0):
     d, hq, hk = w.head_dim, w.n_q_heads, w.n_kv_heads
     q, k, v, pos = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["pos"])
     T = int(pos.numel())
@@ -315,7 +316,7 @@ def run_rotate_qkv(w, inp, angles, b, g, *, debug=True):
                "v_rot_f32": torch.empty((T, hk, d), dtype=torch.float32, device=DEV),
                "v_scale_f32": torch.empty((T, hk, d // g), dtype=torch.float32, device=DEV)}
     q_out = torch.empty_like(q)
-    rrp.rotate_quantize_qkv(shape_of(w), q, k, v, pos, support_b=b, group=g, k_codes=kc, k_scales=ks,
+    rrp.rotate_quantize_qkv(shape_of(w, 0, ah), q, k, v, pos, support_b=b, group=g, k_codes=kc, k_scales=ks,
                             v_codes=vc, v_scales=vs, angles=None if angles is None else to_dev(angles), q_out=q_out,
                             slot_mapping=to_dev(inp.get("slot_mapping")), n_slots=n_slots, **dbg)
     torch.cuda.synchronize()
@@ -386,11 +387,12 @@ def test_rotate_qkv_prefill_128k_sampled():
 # calibration
 # ---------------------------------------------------------------------------
 
-def run_calib(w, q, k, pos, estimator, layout=0, moments=None):
+def run_calib(w, q, k, pos, estimator, layout=0, moments=None, ah=0):
     d = w.head_dim
-    mom = moments if moments is not None else rrp.new_moments(d, DEV)
-    ang = torch.empty(d // 2, dtype=torch.float32, device=DEV)
-    rrp.calibrate_angles(shape_of(w, layout), None if q is None else to_dev(q), to_dev(k), to_dev(pos),
+    A = ah if ah > 1 else 1
+    mom = moments if moments is not None else rrp.new_moments(d, DEV, n_sets=A)
+    ang = torch.empty((d // 2,) if A == 1 else (A, d // 2), dtype=torch.float32, device=DEV)
+    rrp.calibrate_angles(shape_of(w, layout, ah), None if q is None else to_dev(q), to_dev(k), to_dev(pos),
                          moments=mom, estimator=estimator, angles_out=ang)
     torch.cuda.synchronize()
     return mom.cpu().numpy(), ang.cpu().numpy()
@@ -451,9 +453,9 @@ def test_calibration_is_deterministic():
 STAT_TOL = np.array([1e-9, 1e-11, 1e-11, 1e-13, 1e-11])
 
 
-def run_stats(w, k, pos, angles, b, g):
+def run_stats(w, k, pos, angles, b, g, ah=0):
     st = torch.empty(8, dtype=torch.float64, device=DEV)
-    rrp.quant_error_stats(shape_of(w), to_dev(k), to_dev(pos), support_b=b, group=g, stats_out=st,
+    rrp.quant_error_stats(shape_of(w, 0, ah), to_dev(k), to_dev(pos), support_b=b, group=g, stats_out=st,
                           angles=None if angles is None else to_dev(angles))
     torch.cuda.synchronize()
     return st.cpu().numpy()
@@ -484,10 +486,10 @@ def test_quant_error_stats_is_deterministic():
     assert np.array_equal(a, b)
 
 
-def run_sweep(w, k, pos, angles, g):
+def run_sweep(w, k, pos, angles, g, ah=0):
     nb = len(rrp.sweep_supports(w.head_dim))
     st = torch.empty((nb, 8), dtype=torch.float64, device=DEV)
-    rrp.quant_error_sweep(shape_of(w), to_dev(k), to_dev(pos), group=g, stats_out=st,
+    rrp.quant_error_sweep(shape_of(w, 0, ah), to_dev(k), to_dev(pos), group=g, stats_out=st,
                           angles=None if angles is None else to_dev(angles))
     torch.cuda.synchronize()
     return st.cpu().numpy()
@@ -536,3 +538,115 @@ def test_quant_error_sweep_prefill_128k_properties():
         assert abs(sw[j, 1] - sw[0, 1]) <= 1e-11 * sw[0, 1]
         assert sw[j, 6] == w.n_tokens * w.n_kv_heads and sw[j, 7] == b
     print("rel_err by b", [round(float(np.sqrt(x[0] / x[1])), 5) for x in sw])
+
+
+# ---------------------------------------------------------------------------
+# per-key-head angle sets (one set of pair angles per key head; each query head
+# uses its key head's set)
+# ---------------------------------------------------------------------------
+
+def random_angle_sets(w, seed):
+    return np.stack([random_angles(w.n_pairs, seed + 17 * h) for h in range(w.n_kv_heads)])
+
+
+@pytest.mark.parametrize("n,est", [(2, "default"), (2, "k_only"), (2, "stream_balanced"), (3, "default"),
+                                   (4, "default"), (5, "k_only")])
+def test_per_head_calibration_parity(n, est):
+    w = W.WORKLOADS[n]
+    inp = inputs(n)
+    src = inp["calib"] if inp["calib"] is not None else inp
+    q = src["q"] if est != "k_only" else None
+    hk = w.n_kv_heads
+    mom_g, ang_g = run_calib(w, q, src["k"], src["pos"], est, ah=hk)
+    assert mom_g.shape == (hk, w.n_pairs, 2, 6) and ang_g.shape == (hk, w.n_pairs)
+    mom_r = O.calibrate_moments(oshape_of(w, ah=hk), q, src["k"], src["pos"])
+    phi64, _, abc = O.angles_from_moments(mom_r, EST[est])
+    worst = C.compare_moments(mom_g, mom_r)
+    rep = C.compare_angles(ang_g.reshape(-1), phi64.reshape(-1), abc.reshape(-1, 3))
+    # the sets do differ from head to head, and from the shared angles
+    _, ang_shared = run_calib(w, q, src["k"], src["pos"], est)
+    assert np.max(C.angle_diff(ang_g, ang_shared[None, :])) > 1e-3
+    print(f"workload {n} {est} per head: moments {worst:.2e} {rep}")
+
+
+def test_per_head_calibration_accumulates_across_calls():
+    w, inp = W.WORKLOADS[2], inputs(2)
+    hk = w.n_kv_heads
+    mom_all, ang_all = run_calib(w, inp["q"], inp["k"], inp["pos"], "default", ah=hk)
+    mom = rrp.new_moments(w.head_dim, DEV, n_sets=hk)
+    run_calib(w, inp["q"][:900], inp["k"][:900], inp["pos"][:900], "default", moments=mom, ah=hk)
+    mom2, ang2 = run_calib(w, inp["q"][900:], inp["k"][900:], inp["pos"][900:], "default", moments=mom, ah=hk)
+    C.compare_moments(mom2, mom_all, rel=1e-13)
+    assert np.max(C.angle_diff(ang2, ang_all)) < 1e-6
+
+
+@pytest.mark.parametrize("n,b", [(2, 2), (2, 16), (2, 64), (3, 2), (3, 128), (5, 128)])
+def test_per_head_rotate_parity(n, b):
+    w, inp = W.WORKLOADS[n], inputs(n)
+    T = min(w.n_tokens, 2048)
+    sub = {k: (v[:T] if isinstance(v, np.ndarray) and k != "slot_mapping" else v) for k, v in inp.items()}
+    if inp.get("slot_mapping") is not None:
+        sub["slot_mapping"] = inp["slot_mapping"][:T]
+    else:
+        sub["n_slots"] = T
+    ang = random_angle_sets(w, 1000 + n)
+    out = run_rotate(w, sub, ang, b, w.group, ah=w.n_kv_heads)
+    print(f"workload {n} b={b} per head:", check_rotate(w, sub, out, ang, b, w.group, np.arange(T), ah=w.n_kv_heads))
+
+
+def test_per_head_rotate_prefill_128k_sampled():
+    """The 131072-token prefill with one angle set per key head, at full size (the
+    benchmark's launch shape), checked on 2048 sampled tokens."""
+    w, inp = W.WORKLOADS[4], inputs(4)
+    ang = random_angle_sets(w, 1004)
+    out = run_rotate(w, inp, ang, 128, 128, debug=False, ah=w.n_kv_heads)
+    print(check_rotate(w, inp, out, ang, 128, 128, sample_tokens(w.n_tokens, 2048, 24), ah=w.n_kv_heads))
+
+
+def test_per_head_identical_sets_equal_the_shared_path():
+    """Every key head given the same set reproduces the shared-angle launch bit for bit."""
+    w, inp = W.WORKLOADS[3], inputs(3)
+    shared = random_angles(w.n_pairs, 1100)
+    sets = np.tile(shared, (w.n_kv_heads, 1))
+    for b in (2, 128):
+        a = run_rotate(w, inp, shared, b, 128)
+        c = run_rotate(w, inp, sets, b, 128, ah=w.n_kv_heads)
+        for key in ("q_out", "codes", "scales", "q_rot_f32", "k_rot_f32", "k_scale_f32"):
+            x, y = a[key], c[key]
+            if x.dtype == torch.bfloat16:
+                x, y = x.view(torch.int16), y.view(torch.int16)
+            assert torch.equal(x, y), (b, key)
+    st_a = run_stats(w, inp["k"], inp["pos"], shared, 128, 128)
+    st_c = run_stats(w, inp["k"], inp["pos"], sets, 128, 128, ah=w.n_kv_heads)
+    assert np.array_equal(st_a, st_c)
+
+
+@pytest.mark.parametrize("n,b,g", [(2, 64, 64), (3, 128, 128), (3, 2, 16)])
+def test_per_head_rotate_qkv_parity(n, b, g):
+    w = W.WORKLOADS[n]
+    T = min(w.n_tokens, 1024)
+    inp = vinputs(n, T)
+    ang = random_angle_sets(w, 1200 + n)
+    hk = w.n_kv_heads
+    out = run_rotate_qkv(w, inp, ang, b, g, ah=hk)
+    rep_k = check_rotate(w, inp, out, ang, b, g, np.arange(T), ah=hk)
+    rep_v = check_v(w, inp, out, g, np.arange(T))
+    print(f"workload {n} b={b} g={g} per head: K {rep_k} V {rep_v}")
+
+
+@pytest.mark.parametrize("n,g", [(2, 64), (3, 128), (3, 8)])
+def test_per_head_stats_and_sweep_parity(n, g):
+    w = W.WORKLOADS[n]
+    T = min(w.n_tokens, 1024)
+    inp = W.make_inputs(n, n_tokens=T)
+    hk = w.n_kv_heads
+    ang = random_angle_sets(w, 1300 + n)
+    sw = run_sweep(w, inp["k"], inp["pos"], ang, g, ah=hk)
+    for j, b in enumerate(rrp.sweep_supports(w.head_dim)):
+        r = O.quant_error_stats(oshape_of(w, ah=hk), inp["k"], inp["pos"], ang, b, g)
+        one = run_stats(w, inp["k"], inp["pos"], ang, b, g, ah=hk)
+        for got in (sw[j], one):
+            rel = np.abs(got[:5] - r[:5]) / np.maximum(np.abs(r[:5]), 1e-300)
+            assert np.all(rel <= STAT_TOL), (b, got, r, rel)
+            assert got[5] == r[5] and got[6] == r[6]
+    print(f"workload {n} g={g} per head: rel_err by b", [round(float(np.sqrt(x[0] / x[1])), 5) for x in sw])

@@ -33,7 +33,7 @@ METRIC = "Q/K rotate+INT4-quantise tokens/sec and achieved HBM GB/s (% of peak),
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rotate_quantize_prefill128k_traffic.json")
 KERNEL_SOURCES = ["rotation_rope_pair_amd/csrc/rrp_device.hpp", "rotation_rope_pair_amd/csrc/rrp_rotate.hip",
-                  "rotation_rope_pair_amd/csrc/rrp_rotate.hpp"]
+                  "rotation_rope_pair_amd/csrc/rrp_rotate.hpp", "rotation_rope_pair_amd/csrc/rrp_rotate_kernel.hpp"]
 
 
 def kernel_source_hash():
@@ -80,9 +80,12 @@ def to_device_bf16(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
 
-def decode_latency_us(dev, stream, reps=50):
+def decode_latency_us(dev, stream, reps=200):
     """Per-launch time of the 256-token Mistral-shaped decode batch (slot scatter
-    into a 256 x 32768-slot KV4 cache)."""
+    into a 256 x 32768-slot KV4 cache), two ways: launches through the Python
+    binding (its argument checks cost more host time than the kernel takes), and
+    back-to-back calls of the C entry point with the arguments marshalled once,
+    which keeps the GPU busy and so times the kernel itself."""
     import torch
     import rotation_rope_pair_amd as rrp
     from rotation_rope_pair_amd import workloads as W
@@ -99,15 +102,27 @@ def decode_latency_us(dev, stream, reps=50):
     def launch():
         rrp.rotate_quantize_qk(shape5, q5, k5, pos5, support_b=128, group=w5.group, k_codes=c5, k_scales=s5,
                                angles=a5, q_out=q5o, slot_mapping=sm5, n_slots=inp5["n_slots"])
-    for _ in range(5):
-        launch()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        launch()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps * 1e3
+    from rotation_rope_pair_amd import _abi, api
+    L = _abi.load()
+    args = api._rotate_args(shape5, q5, k5, None, pos5, 128, w5.group, c5, s5, None, None, a5, q5o, sm5,
+                            inp5["n_slots"], None, None, None, None, None, None)
+
+    def launch_c():
+        _abi.check("rrp_rotate_quantize_qk", L.rrp_rotate_quantize_qk(*args))
+    out = {}
+    for key, fn in (("decode256_rotate_quantize_us", launch_c),
+                    ("decode256_rotate_quantize_us_python_binding", launch)):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[key] = e0.elapsed_time(e1) / reps * 1e3
+    return out
 
 
 def qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b, g, reps=50):
@@ -318,7 +333,7 @@ def main():
     copy_ref = {"kernel": "torch device-to-device copy of Q (bf16)", "bytes_read_plus_written": copy_bytes,
                 "ms": copy_ms, "GBs": copy_bytes / (copy_ms * 1e-3) / 1e9}
     if not args.hot_path_only:
-        supporting["decode256_rotate_quantize_us"] = decode_latency_us(dev, stream)
+        supporting.update(decode_latency_us(dev, stream))
         supporting.update(qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b, g))
         supporting.update(per_head_timing(w, q, k, pos, q_out, codes, scales, dev, stream, b, g))
         supporting.update(decode_scores_timing(dev, stream))

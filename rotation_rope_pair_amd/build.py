@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librrp.so")
-SOURCES = ["rrp_abi.hip", "rrp_rotate.hip", "rrp_calib.hip", "rrp_stats.hip", "rrp_decode.hip"]
+SOURCES = ["rrp_rotate.hip", "rrp_rotate_split.hip", "rrp_stats.hip", "rrp_decode.hip", "rrp_calib.hip",
+           "rrp_abi.hip"]
 ARCH = os.environ.get("RRP_OFFLOAD_ARCH", "gfx950")
 
 
@@ -53,7 +54,7 @@ def _compile(src, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", LIB + ".tmp"]
     if verbose:

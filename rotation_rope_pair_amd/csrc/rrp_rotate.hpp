@@ -37,6 +37,7 @@ struct RotateArgs {
     int32_t support_b;
     int32_t group;
     int32_t angle_sets;  // 1: one set shared by all heads; n_kv_heads: one per key head
+    int32_t split;       // waves per token (set by the launcher; > 1 for small batches)
     double rsqrt_b;
     double rsqrt_v;  // 1 / sqrt(head_dim)
     float inv_freq[kMaxPairs];
@@ -44,5 +45,7 @@ struct RotateArgs {
 
 // dtype: 0 fp32, 1 bf16; layout: 0 half-split, 1 interleaved.
 hipError_t launch_rotate_quantize(const RotateArgs& a, int dtype, int head_dim, int layout, hipStream_t st);
+// The small-batch family (0 < n_tokens < 4096), called by launch_rotate_quantize.
+hipError_t launch_rotate_quantize_split(const RotateArgs& a, int dtype, int head_dim, int layout, hipStream_t st);
 
 }  // namespace rrp

@@ -127,6 +127,7 @@ int rotate_quantize(const rrp_shape* shape, int32_t dtype, const void* q, const 
     a.support_b = support_b;
     a.group = group;
     a.angle_sets = angles != nullptr ? angle_sets(shape) : 1;
+    a.q_set_scale = shape->n_q_heads > 0 ? (float)a.angle_sets / (float)shape->n_q_heads : 0.0f;
     a.rsqrt_b = 1.0 / sqrt((double)support_b);
     a.rsqrt_v = 1.0 / sqrt((double)shape->head_dim);
     fill_inv_freq(shape, a.inv_freq);
@@ -183,7 +184,8 @@ RRP_EXPORT int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const
     if (n_tokens > 0) {
         int nbq = 0, nbk = 0;
         const bool with_q = q != nullptr && shape->n_q_heads > 0;
-        const int nb = rrp::calib_blocks(n_tokens, with_q, shape->n_q_heads, shape->n_kv_heads, f.n_sets, &nbq, &nbk);
+        const int nb = rrp::calib_blocks(n_tokens, with_q, shape->n_q_heads, shape->n_kv_heads, shape->head_dim, f.n_sets,
+                                         &nbq, &nbk);
         if (scratch.alloc((size_t)nb * P * 5 * sizeof(double), s) != hipSuccess) return RRP_ERR_HIP;
         rrp::CalibArgs a{};
         a.q = q;

@@ -279,9 +279,15 @@ hipError_t launch_t(const CalibArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int n_sets, int* nbq, int* nbk) {
+#ifndef RRP_CALIB_TABLE_WEIGHT
+#define RRP_CALIB_TABLE_WEIGHT 2
+#endif
+
+int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, int n_sets, int* nbq, int* nbk) {
     // About 8 tokens per wave per stream, at most kMaxCalibBlocks blocks over all
-    // sets, split between the streams in proportion to their rows.
+    // sets.  The streams share a set's blocks in proportion to their work per
+    // token: the row passes of the set's heads plus the token's table (worth
+    // about RRP_CALIB_TABLE_WEIGHT passes).
     int64_t want = (n_tokens * (with_q ? 2 : 1) + 31) / 32;
     if (want > kMaxCalibBlocks) want = kMaxCalibBlocks;
     want = (want + n_sets - 1) / n_sets;  // per set
@@ -291,7 +297,10 @@ int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int n_sets, int*
         *nbq = 0;
         *nbk = total;
     } else {
-        int q = (int)((int64_t)total * hq / (hq + hk));
+        const int rp = 512 / head_dim;  // rows per pass
+        const int64_t wq = (hq / n_sets + rp - 1) / rp + RRP_CALIB_TABLE_WEIGHT;
+        const int64_t wk = (hk / n_sets + rp - 1) / rp + RRP_CALIB_TABLE_WEIGHT;
+        int q = (int)((int64_t)total * wq / (wq + wk));
         if (q < 1) q = 1;
         if (q > total - 1) q = total - 1;
         *nbq = q;

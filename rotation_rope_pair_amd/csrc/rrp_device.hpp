@@ -16,6 +16,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "rrp_rotate.hpp"  // kMaxAngleSets
 
 namespace rrp {
 
@@ -246,20 +247,27 @@ __device__ __forceinline__ void token_tables(float2* tab32, double2* tab64, int 
 
 // ---------------------------------------------------------------------------
 // Per-head angle sets: one set of pair angles per key head (query heads use
-// their key head's set).  The block keeps cos / sin of every set's angles in
-// LDS (phi[set * P + k]); each token's tables are built for every set:
-// tab64[set * P + k], tab32[set * P + k] (tab32 may be null).
+// their key head's set).  Tables are pair-major, entry (k, set) at
+// k * kSetStride + set: a lane's sets sit together, the rows of one pass
+// (different sets, same pairs) read neighbouring entries, a pair's offset is a
+// compile-time multiple of the lane's base, and the padding entry spreads the
+// lanes' pairs over the LDS banks.  The block keeps
+// cos / sin of every set's angles in LDS (phi); each token's composed fp64
+// tables are built for every set (tab64).
 // ---------------------------------------------------------------------------
-// cos / sin of angles[0 .. n) into phi (block-wide; ends with a block barrier).
-__device__ __forceinline__ void load_angle_sets(double2* phi, const float* angles, int n) {
-    for (int e = (int)threadIdx.x; e < n; e += (int)blockDim.x) {
+// cos / sin of angles[set][k] (n_sets x P floats) into phi[k * kSetStride + set]
+// (block-wide; ends with a block barrier).
+template <int P>
+__device__ __forceinline__ void load_angle_sets(double2* phi, const float* angles, int n_sets) {
+    for (int e = (int)threadIdx.x; e < n_sets * P; e += (int)blockDim.x) {
         double sv = 0.0, cv = 1.0;
         if (angles != nullptr) sincos_f64_of_f32(angles[e], sv, cv);
-        phi[e] = make_double2(cv, sv);
+        phi[(e % P) * kSetStride + e / P] = make_double2(cv, sv);
     }
     __syncthreads();
 }
 
+// tab32 (the same entries rounded to fp32) may be null.
 template <int D, bool FOLD>
 __device__ __forceinline__ void token_tables_sets(float2* tab32, double2* tab64, int lane, int p, float invf,
                                                   const double2* phi, int n_sets, double rs) {
@@ -269,11 +277,11 @@ __device__ __forceinline__ void token_tables_sets(float2* tab32, double2* tab64,
         double sa, ca;
         sincos_f64_of_f32(rope_angle_f32(p, invf), sa, ca);
         for (int g = 0; g < n_sets; ++g) {
-            const double2 cs = phi[g * P + lane];
+            const double2 cs = phi[lane * kSetStride + g];
             const double C = (ca * cs.x - sa * cs.y) * rs, S = (sa * cs.x + ca * cs.y) * rs;
             const double e0 = FOLD ? C + S : C, e1 = FOLD ? C - S : S;
-            tab64[g * P + lane] = make_double2(e0, e1);
-            if (tab32 != nullptr) tab32[g * P + lane] = make_float2((float)e0, (float)e1);
+            tab64[lane * kSetStride + g] = make_double2(e0, e1);
+            if (tab32 != nullptr) tab32[lane * kSetStride + g] = make_float2((float)e0, (float)e1);
         }
     }
     wave_lds_sync();

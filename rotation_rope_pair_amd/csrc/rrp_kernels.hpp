@@ -80,7 +80,7 @@ struct DecodeArgs {
 };
 
 
-int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int n_sets, int* nbq, int* nbk);
+int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, int n_sets, int* nbq, int* nbk);
 hipError_t launch_calibrate(const CalibArgs& a, int dtype, int head_dim, int layout, hipStream_t st);
 hipError_t launch_calibrate_final(const CalibFinalArgs& a, hipStream_t st);
 

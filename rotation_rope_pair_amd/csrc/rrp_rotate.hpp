@@ -9,6 +9,9 @@ namespace rrp {
 
 constexpr int kMaxPairs = 64;     // head_dim <= 128
 constexpr int kMaxAngleSets = 8;  // per-head angle sets held in LDS per token
+// Entry stride of a pair in the per-set LDS tables (pair-major, one padding
+// entry so that neighbouring lanes' pairs fall in different LDS banks).
+constexpr int kSetStride = kMaxAngleSets + 1;
 
 // RoPE frequencies travel in the kernel argument block: every lane reads its
 // own pair's entry, so no device table has to be allocated or kept.
@@ -38,6 +41,7 @@ struct RotateArgs {
     int32_t group;
     int32_t angle_sets;  // 1: one set shared by all heads; n_kv_heads: one per key head
     int32_t split;       // waves per token (set by the launcher; > 1 for small batches)
+    float q_set_scale;   // angle sets / Hq: query head h uses set floor((h + 1/2) * q_set_scale)
     double rsqrt_b;
     double rsqrt_v;  // 1 / sqrt(head_dim)
     float inv_freq[kMaxPairs];

@@ -98,12 +98,24 @@ template <int R> struct Depth {
 // BT: compile-time Hadamard support (BT == D, the full-head case) or 0 (runtime b).
 // HAS_V: also turn the V rows by the full-head Hadamard and quantise them into
 // the V half of the cache (no RoPE, no pair rotation).
-// PH: one angle set per key head (a.angle_sets of them); query head h uses set
-// h * sets / Hq, key head kh set kh * sets / Hkv.  Blocks then hold at most two
-// waves, so the per-set tables stay within 32 KB of LDS per block.
+// PH: one angle set per key head (a.angle_sets = Hkv of them); query head h uses
+// set h * sets / Hq, key head kh set kh.  Each wave keeps the fp64 tables of
+// every set (9 KB) and Q rounds its entries to fp32 as it reads them (the values
+// of the shared path's fp32 table); with the block's cos / sin of the sets
+// (9 KB), blocks of kPerSetWaves = 4 waves take 46 KB, three per CU.
 // SPLIT: each token's row passes are shared by a.split waves (small batches).
+#ifndef RRP_PH_WAVES
+#define RRP_PH_WAVES 4
+#endif
+#ifndef RRP_PH_Q64
+#define RRP_PH_Q64 1
+#endif
+constexpr int kPerSetWaves = RRP_PH_WAVES;
+constexpr bool kPerSetQ64 = RRP_PH_Q64;  // Q reads the fp64 per-set tables
+
 template <typename E, int D, int LAYOUT, bool SMALLG, int BT, bool HAS_V, bool PH, bool SPLIT>
-__global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, PH ? 64 * kPerSetWaves : 256)))
+void rotate_quantize_kernel(const RotateArgs a) {
     using G = Geo<E, D>;
     using LM = LaneMap<G::L>;
     constexpr int CE = G::CE, P = G::P, R = G::R;
@@ -111,11 +123,10 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
     constexpr int ROWB = D * EB;
     constexpr int MQ = Depth<R>::Q, MK = Depth<R>::K;
     constexpr bool FOLD = (LAYOUT == 0) && (BT == D);
-    constexpr int WMAX = PH ? 2 : 4;             // waves per block
-    constexpr int NA = PH ? kMaxAngleSets : 1;   // angle sets held per token
-    __shared__ float2 tab32_all[WMAX][NA * P];
-    __shared__ double2 tab64_all[WMAX][NA * P];
-    __shared__ double2 phi_all[PH ? NA * P : 1];
+    constexpr int WMAX = PH ? kPerSetWaves : 4;  // waves per block
+    __shared__ float2 tab32_all[WMAX][PH ? (kPerSetQ64 ? 1 : kSetStride * P) : P];
+    __shared__ double2 tab64_all[WMAX][PH ? kSetStride * P : P];
+    __shared__ double2 phi_all[PH ? kSetStride * P : 1];
 
     const int lane = (int)__lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -126,7 +137,7 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
     double2* tab64 = tab64_all[wave];
 
     double cphi = 1.0, sphi = 0.0;
-    if constexpr (PH) load_angle_sets(phi_all, a.angles, a.angle_sets * P);
+    if constexpr (PH) load_angle_sets<P>(phi_all, a.angles, a.angle_sets);
     else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
     const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
     // Rows are loaded permuted (lane s holds position s ^ perm), see fwht_row.
@@ -134,6 +145,10 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
     const int s_src_v = s ^ lane_perm_mask<D, CE>(D);  // V: full-head support
     int kidx[CE];
     pair_index_of_lane<D, LAYOUT, CE>(s_src, kidx);
+    if constexpr (PH) {
+#pragma unroll
+        for (int j = 0; j < CE; ++j) kidx[j] *= kSetStride;  // pair-major per-set tables
+    }
 
     const int hq = a.hq_rows, hk = a.hk;
     const int nq = (hq + R - 1) / R, nk = (hk + R - 1) / R;
@@ -190,7 +205,9 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
                     load_row_chunks<E, D>(vt + (v0 + i) * R * ROWB + ld_off, s_src_v, rv[i]);
         }
 
-        if constexpr (PH) token_tables_sets<D, FOLD>(tab32, tab64, lane, p, invf, phi_all, a.angle_sets, a.rsqrt_b);
+        if constexpr (PH)
+            token_tables_sets<D, FOLD>(kPerSetQ64 ? nullptr : tab32, tab64, lane, p, invf, phi_all, a.angle_sets,
+                                       a.rsqrt_b);
         else token_tables<D, FOLD>(tab32, tab64, lane, p, invf, cphi, sphi, a.rsqrt_b);
 
         // ---- Q rows (fp32) ----
@@ -210,7 +227,14 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
                 float x[2][CE];
                 unpack_chunk<E, CE>(rq[i][0], x[0]);
                 unpack_chunk<E, CE>(rq[i][1], x[1]);
-                rotate_lds<LAYOUT, FOLD>(x, PH ? tab32 + (h * a.angle_sets / a.hq) * P : tab32, kidx);
+                if constexpr (PH) {
+                    // set of query head h: floor((h + 1/2) * sets / Hq), exact in fp32
+                    const int qset = (int)(((float)h + 0.5f) * a.q_set_scale);
+                    if constexpr (kPerSetQ64) rotate_lds<LAYOUT, FOLD>(x, tab64 + qset, kidx);
+                    else rotate_lds<LAYOUT, FOLD>(x, tab32 + qset, kidx);
+                } else {
+                    rotate_lds<LAYOUT, FOLD>(x, tab32, kidx);
+                }
                 fwht_row<D, CE, BT, FOLD>(x, a.support_b, s);
                 if (qo) {
 #pragma unroll
@@ -251,7 +275,7 @@ __global__ __launch_bounds__(256) void rotate_quantize_kernel(const RotateArgs a
                 for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                     for (int i2 = 0; i2 < CE; ++i2) x[ch][i2] = (KV)xf[ch][i2];
-                const int kset = PH ? (h * a.angle_sets / hk) * P : 0;
+                const int kset = PH ? h : 0;  // key head h uses set h
                 if constexpr (RRP_K_FP64) rotate_lds<LAYOUT, FOLD>(x, tab64 + kset, kidx);
                 else rotate_lds<LAYOUT, FOLD>(x, tab32 + kset, kidx);
                 fwht_row<D, CE, BT, FOLD>(x, a.support_b, s);
@@ -327,7 +351,7 @@ hipError_t launch_t(const RotateArgs& args, hipStream_t st) {
     RotateArgs a = args;
     const bool ph = a.angle_sets > 1;
     // Small batches: one wave per block so the work spreads over all CUs.
-    const int wpb = a.n_tokens >= 4096 ? (ph ? 2 : 4) : 1;
+    const int wpb = a.n_tokens >= 4096 ? (ph ? kPerSetWaves : 4) : 1;
     a.split = 1;
     if constexpr (SPLIT) {
         constexpr int R = Geo<E, D>::R;

@@ -124,8 +124,8 @@ __device__ __forceinline__ void block_stats_partials(StatAcc acc, int set, doubl
     }
 }
 
-// PH: one angle set per key head (a.angle_sets of them), key head kh using set
-// kh * sets / Hkv; the fp64 tables of every set are kept per wave.
+// PH: one angle set per key head (a.angle_sets = Hkv of them), key head kh using
+// set kh; the fp64 tables of every set are kept per wave (pair-major).
 template <typename E, int D, int LAYOUT, int BT, bool SMALLG, bool PH>
 __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     using G = Geo<E, D>;
@@ -134,10 +134,9 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr size_t ROWB = (size_t)D * EB;
     constexpr bool FOLD = (LAYOUT == 0) && (BT == D);
-    constexpr int NA = PH ? kMaxAngleSets : 1;  // angle sets held per token
     __shared__ float2 tab32_all[4][PH ? 1 : P];  // fp32 tables (unused by per-set tables)
-    __shared__ double2 tab64_all[4][NA * P];
-    __shared__ double2 phi_all[PH ? NA * P : 1];
+    __shared__ double2 tab64_all[4][PH ? kSetStride * P : P];
+    __shared__ double2 phi_all[PH ? kSetStride * P : 1];
     __shared__ double red[4][kNStat];
 
     const int lane = (int)__lane_id();
@@ -149,12 +148,16 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     double2* tab64 = tab64_all[wave];
 
     double cphi = 1.0, sphi = 0.0;
-    if constexpr (PH) load_angle_sets(phi_all, a.angles, a.angle_sets * P);
+    if constexpr (PH) load_angle_sets<P>(phi_all, a.angles, a.angle_sets);
     else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
     const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
     const int s_src = s ^ lane_perm_mask<D, CE>(BT ? BT : a.support_b);  // permuted loads, see fwht_row
     int kidx[CE];
     pair_index_of_lane<D, LAYOUT, CE>(s_src, kidx);
+    if constexpr (PH) {
+#pragma unroll
+        for (int j = 0; j < CE; ++j) kidx[j] *= kSetStride;  // pair-major per-set tables
+    }
     const unsigned char* kb = static_cast<const unsigned char*>(a.k);
     const int npass = (a.hk + R - 1) / R;
     const int g = a.group;
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int i2 = 0; i2 < CE; ++i2) y[ch][i2] = (double)yf[ch][i2];
-            rotate_lds<LAYOUT, FOLD>(y, PH ? tab64 + ((ps * R + grp) * a.angle_sets / a.hk) * P : tab64, kidx);
+            rotate_lds<LAYOUT, FOLD>(y, PH ? tab64 + (ps * R + grp) : tab64, kidx);
             fwht_row<D, CE, BT, FOLD>(y, a.support_b, s);
             add_row_stats<D, CE, SMALLG>(y, g, s, acc);
         }
@@ -287,10 +290,9 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr size_t ROWB = (size_t)D * EB;
     constexpr int NJ = J1 - J0;
-    constexpr int NA = PH ? kMaxAngleSets : 1;  // angle sets held per token
     __shared__ float2 tab32_all[4][PH ? 1 : P];  // fp32 tables (unused by per-set tables)
-    __shared__ double2 tab64_all[4][NA * P];
-    __shared__ double2 phi_all[PH ? NA * P : 1];
+    __shared__ double2 tab64_all[4][PH ? kSetStride * P : P];
+    __shared__ double2 phi_all[PH ? kSetStride * P : 1];
     __shared__ double red[4][kNStat];
 
     const int lane = (int)__lane_id();
@@ -302,11 +304,15 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
     double2* tab64 = tab64_all[wave];
 
     double cphi = 1.0, sphi = 0.0;
-    if constexpr (PH) load_angle_sets(phi_all, a.angles, a.angle_sets * P);
+    if constexpr (PH) load_angle_sets<P>(phi_all, a.angles, a.angle_sets);
     else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
     const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
     int kidx[CE];
     pair_index_of_lane<D, LAYOUT, CE>(s, kidx);  // natural chunk order
+    if constexpr (PH) {
+#pragma unroll
+        for (int j = 0; j < CE; ++j) kidx[j] *= kSetStride;  // pair-major per-set tables
+    }
     const unsigned char* kb = static_cast<const unsigned char*>(a.k);
     const int npass = (a.hk + R - 1) / R;
     const int g = a.group;
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int i2 = 0; i2 < CE; ++i2) y[ch][i2] = (double)yf[ch][i2];
-            rotate_lds<LAYOUT, false>(y, PH ? tab64 + ((ps * R + grp) * a.angle_sets / a.hk) * P : tab64, kidx);
+            rotate_lds<LAYOUT, false>(y, PH ? tab64 + (ps * R + grp) : tab64, kidx);
             SweepRest<D, CE, SMALLG, 0, J0, J1>::run(y, g, s, acc);
         }
         cur[0] = nxt[0];

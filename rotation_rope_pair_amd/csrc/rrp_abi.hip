@@ -281,6 +281,8 @@ RRP_EXPORT int rrp_decode_scores(const rrp_shape* shape, int32_t dtype, const vo
     const int hq = shape->n_q_heads, hk = shape->n_kv_heads, d = shape->head_dim;
     if (hq < 1 || hq % hk != 0) return RRP_ERR_INVALID_ARG;
     if (hq / hk > 16) return RRP_ERR_UNSUPPORTED;  // one MFMA column per query head of a key head
+    // a wave's chunk of keys is addressed by 32-bit offsets from its first row
+    if ((int64_t)rrp::decode_chunk_keys() * hk * (d / 2) >= ((int64_t)1 << 31)) return RRP_ERR_UNSUPPORTED;
     if (!is_pow2(group) || group < 2 || group > d) return RRP_ERR_INVALID_ARG;
     if (n_seqs < 0 || n_slots < 0 || max_len < 0) return RRP_ERR_INVALID_ARG;
     if (n_seqs == 0 || max_len == 0) return RRP_OK;

@@ -47,19 +47,33 @@ constexpr int kTilesPerStep = RRP_DECODE_TILES_PER_STEP;  // 16-key tiles loaded
 __device__ __forceinline__ constexpr int elem_channel(int e) { return (e >> 1) + 4 * (e & 1); }
 
 // Eight two's-complement INT4 codes (nibble n = channel n) -> half8 in element order.
-// Offset binary (x ^ 8) under the f16 exponent of 1024 gives 1024 + code + 8
-// exactly; subtracting 1032 leaves the code.
+// Each code is made offset binary (x ^ 8, 0..15) and dropped into the mantissa of
+// an f16 whose exponent makes the nibble's lowest bit worth 1: nibbles at bits
+// 0-3 of a 16-bit half under the exponent of 1024 (value 1024 + n), nibbles at
+// bits 4-7 under the exponent of 64 (value 64 + n).  One packed subtraction of
+// 1032 or 72 then leaves the code exactly.  A shift by 8 brings channels 2, 3
+// (and 6, 7 in the high half) to the same places, so a word costs one shift,
+// four bit operations and four packed subtractions.
+// nibble ^ 8 under the mask, the magic exponent elsewhere: one three-input bit
+// operation (the xor is folded in, since the magic and the mask do not overlap).
+__device__ __forceinline__ unsigned nib_magic(unsigned w, unsigned mask, unsigned magic) {
+    const unsigned k = magic | (0x88888888u & mask);
+    return ((w ^ k) & mask) | (k & ~mask);
+}
+
 __device__ __forceinline__ half8 codes_to_half8(unsigned w) {
-    const unsigned x = w ^ 0x88888888u;
-    const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const unsigned y = w >> 8;
+    const half2v off_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2v off_hi = {(_Float16)72.0f, (_Float16)72.0f};
+    const half2v h0 = __builtin_bit_cast(half2v, nib_magic(w, 0x000F000Fu, 0x64006400u)) - off_lo;  // channels 0, 4
+    const half2v h1 = __builtin_bit_cast(half2v, nib_magic(w, 0x00F000F0u, 0x54005400u)) - off_hi;  // channels 1, 5
+    const half2v h2 = __builtin_bit_cast(half2v, nib_magic(y, 0x000F000Fu, 0x64006400u)) - off_lo;  // channels 2, 6
+    const half2v h3 = __builtin_bit_cast(half2v, nib_magic(y, 0x00F000F0u, 0x54005400u)) - off_hi;  // channels 3, 7
     half8 r;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const unsigned bits = ((x >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-        const half2v h = __builtin_bit_cast(half2v, bits) - off;
-        r[2 * p] = h[0];
-        r[2 * p + 1] = h[1];
-    }
+    r[0] = h0[0]; r[1] = h0[1];
+    r[2] = h1[0]; r[3] = h1[1];
+    r[4] = h2[0]; r[5] = h2[1];
+    r[6] = h3[0]; r[7] = h3[1];
     return r;
 }
 
@@ -122,7 +136,9 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
     constexpr int KPG = KBM ? GS / LSPAN : 1;   // lane blocks per group (kb-major)
 
     const int lane = (int)__lane_id();
-    const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    // wave-uniform (scalar) indices, so row bases stay in scalar registers
+    const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) +
+                        __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int hk = a.hk;
     const int kvh = (int)(wid % hk);
     const int64_t rest = wid / hk;
@@ -146,37 +162,44 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
     const unsigned char* scales = reinterpret_cast<const unsigned char*>(a.k_scales);
     const size_t code_row = (size_t)D / 2, scale_row = SROW;
     const size_t slot_stride_c = (size_t)hk * code_row, slot_stride_s = (size_t)hk * scale_row;
-    const unsigned char* codes_h = codes + (size_t)kvh * code_row + (KBM ? LSPAN / 2 : 4) * kb;
-    const unsigned char* scales_h = scales + (size_t)kvh * scale_row;
+    const unsigned lane_c = (unsigned)((KBM ? LSPAN / 2 : 4) * kb);  // this lane's bytes in a code row
     // Every key of this wave's chunk sits inside the cache (the usual case):
-    // keys are then only clamped to the chunk, with no 64-bit range checks.
+    // keys are then only clamped to the chunk, and addressed by 32-bit offsets
+    // from the chunk's first row.
     const bool chunk_in_cache = start + k_begin >= 0 && start + k_end <= a.n_slots;
 
     auto body = [&](auto in_cache_tag) {
         constexpr bool FAST = decltype(in_cache_tag)::value;
-        // Row address of `key` inside a half-row base (codes or scales), and whether
-        // the key is real.  Loads are issued unconditionally from a valid address
-        // and zeroed afterwards, so no branch separates them and the waits stay
-        // exact.
-        const unsigned char* codes_s = codes_h + (FAST ? start * (int64_t)slot_stride_c : 0);
-        const unsigned char* scales_s = scales_h + (FAST ? start * (int64_t)slot_stride_s : 0);
-        auto row_of = [&](int key, bool scale_half, bool& ok) -> const unsigned char* {
-            const size_t stride = scale_half ? slot_stride_s : slot_stride_c;
+        // Row address of `key` inside the codes or the scales.  Loads are issued
+        // unconditionally from a valid address and their values are never
+        // masked: a key past the sequence (clamped to its last key) or outside
+        // the cache (read at slot 0) only feeds its own row of the MFMA result,
+        // which is not stored (past the end) or stored as NaN (outside the
+        // cache).  So no branch or wait separates a load from its use.
+        const unsigned char* cbase = codes + (size_t)kvh * code_row;
+        const unsigned char* sbase = scales + (size_t)kvh * scale_row;
+        if constexpr (FAST) {
+            cbase += (start + k_begin) * (int64_t)slot_stride_c;
+            sbase += (start + k_begin) * (int64_t)slot_stride_s;
+        }
+        auto row_of = [&](int key, bool scale_half) -> const unsigned char* {
+            const unsigned char* base = scale_half ? sbase : cbase;
+            const unsigned extra = scale_half ? 0u : lane_c;
             if constexpr (FAST) {
-                ok = key < k_end;
-                const int kc = min(key, k_end - 1);
-                return (scale_half ? scales_s : codes_s) + (size_t)(unsigned)kc * stride;
+                const unsigned stride = (unsigned)(scale_half ? slot_stride_s : slot_stride_c);
+                const unsigned kc = (unsigned)(min(key, k_end - 1) - k_begin);
+                return base + (size_t)(kc * stride + extra);
             } else {
+                const size_t stride = scale_half ? slot_stride_s : slot_stride_c;
                 const int64_t slot = start + key;
-                ok = key < k_end && slot >= 0 && slot < a.n_slots;
-                return (scale_half ? scales_h : codes_h) + (size_t)(ok ? slot : 0) * stride;
+                const bool ok = slot >= 0 && slot < a.n_slots;
+                return base + (size_t)(ok ? slot : 0) * stride + extra;
             }
         };
 
         // A loads for the tile starting at key0: NM words (8 codes each) of key key0 + col.
         auto load_a = [&](int key0, unsigned (&w)[NM]) {
-            bool ok;
-            const unsigned char* row = row_of(key0 + col, false, ok);
+            const unsigned char* row = row_of(key0 + col, false);
             if constexpr (KBM && NM == 4) {
                 const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row));
                 w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
@@ -188,32 +211,24 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
                 for (int m = 0; m < NM; ++m)
                     w[m] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(row + 16 * m));
             }
-            if (!FAST || key0 + 16 > k_end) {
-#pragma unroll
-                for (int m = 0; m < NM; ++m) w[m] = ok ? w[m] : 0u;
-            }
         };
         // Scales of groups [g0, g0 + NS) of the lane's four D keys key0 + 4 kb + r, as fp32.
         auto load_s = [&](int key0, int g0, auto& sv) {
             constexpr int NS = sizeof(sv[0]) / sizeof(float);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                bool ok;
-                const unsigned char* row = row_of(key0 + 4 * kb + r, true, ok) + 2 * g0;
+                const unsigned char* row = row_of(key0 + 4 * kb + r, true) + 2 * g0;
                 if constexpr (NS == 1) {
-                    unsigned short v = *reinterpret_cast<const unsigned short*>(row);
-                    v = ok ? v : (unsigned short)0;
+                    const unsigned short v = *reinterpret_cast<const unsigned short*>(row);
                     sv[r][0] = f16_bits_to_f32(v);
                 } else if constexpr (NS == 2) {
-                    unsigned v = *reinterpret_cast<const unsigned*>(row);
-                    v = ok ? v : 0u;
+                    const unsigned v = *reinterpret_cast<const unsigned*>(row);
                     sv[r][0] = f16_bits_to_f32(v & 0xFFFFu);
                     sv[r][1] = f16_bits_to_f32(v >> 16);
                 } else {
 #pragma unroll
                     for (int q4 = 0; q4 < NS / 4; ++q4) {
-                        u32x2 v = *reinterpret_cast<const u32x2*>(row + 8 * q4);
-                        v = ok ? v : u32x2{0u, 0u};
+                        const u32x2 v = *reinterpret_cast<const u32x2*>(row + 8 * q4);
                         sv[r][4 * q4 + 0] = f16_bits_to_f32(v.x & 0xFFFFu);
                         sv[r][4 * q4 + 1] = f16_bits_to_f32(v.x >> 16);
                         sv[r][4 * q4 + 2] = f16_bits_to_f32(v.y & 0xFFFFu);
@@ -230,18 +245,15 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
         auto load_sw = [&](int key0, unsigned (&sw)[4][NSW]) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                bool ok;
-                const unsigned char* row = row_of(key0 + 4 * kb + r, true, ok);
+                const unsigned char* row = row_of(key0 + 4 * kb + r, true);
                 if constexpr (SROW == 2) {
-                    const unsigned v = *reinterpret_cast<const unsigned short*>(row);
-                    sw[r][0] = ok ? v : 0u;
+                    sw[r][0] = *reinterpret_cast<const unsigned short*>(row);
                 } else if constexpr (SROW == 4) {
-                    const unsigned v = *reinterpret_cast<const unsigned*>(row);
-                    sw[r][0] = ok ? v : 0u;
+                    sw[r][0] = *reinterpret_cast<const unsigned*>(row);
                 } else {
                     const u32x2 v = *reinterpret_cast<const u32x2*>(row);
-                    sw[r][0] = ok ? v.x : 0u;
-                    sw[r][1] = ok ? v.y : 0u;
+                    sw[r][0] = v.x;
+                    sw[r][1] = v.y;
                 }
             }
         };
@@ -258,7 +270,54 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
                 if constexpr (KBM) load_sw(s0 + 16 * tt, sw[tt]);
             }
         };
-        load_step(k_begin, wc, sc);  // the first codes are in flight while the queries are prepared
+        // Steps whose keys all lie in the chunk (FAST, groups of at least d/4):
+        // every lane's row offsets from the step's first row are the same at each
+        // step, so they are computed once and only the wave-uniform base moves.
+        constexpr bool CONST_OFF = FAST && KBM;
+        unsigned off_a[TP], off_s[TP][4];
+#pragma unroll
+        for (int tt = 0; tt < TP; ++tt) {
+            off_a[tt] = (unsigned)((16 * tt + col) * (int)slot_stride_c) + lane_c;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) off_s[tt][r] = (unsigned)((16 * tt + 4 * kb + r) * (int)slot_stride_s);
+        }
+        auto load_step_full = [&](int s0, unsigned (&w)[TP][NM], unsigned (&sw)[TP][4][NSW]) {
+            const unsigned char* cb = cbase + (size_t)(unsigned)(s0 - k_begin) * slot_stride_c;
+            const unsigned char* sb = sbase + (size_t)(unsigned)(s0 - k_begin) * slot_stride_s;
+#pragma unroll
+            for (int tt = 0; tt < TP; ++tt) {
+                if constexpr (NM == 4) {
+                    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cb + off_a[tt]));
+                    w[tt][0] = v.x; w[tt][1] = v.y; w[tt][2] = v.z; w[tt][3] = v.w;
+                } else {
+                    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(cb + off_a[tt]));
+                    w[tt][0] = v.x; w[tt][1] = v.y;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const unsigned char* row = sb + off_s[tt][r];
+                    if constexpr (SROW == 2) {
+                        sw[tt][r][0] = *reinterpret_cast<const unsigned short*>(row);
+                    } else if constexpr (SROW == 4) {
+                        sw[tt][r][0] = *reinterpret_cast<const unsigned*>(row);
+                    } else {
+                        const u32x2 v = *reinterpret_cast<const u32x2*>(row);
+                        sw[tt][r][0] = v.x;
+                        sw[tt][r][1] = v.y;
+                    }
+                }
+            }
+        };
+        auto load_any = [&](int s0, unsigned (&w)[TP][NM], unsigned (&sw)[TP][4][NSW]) {
+            if constexpr (CONST_OFF) {
+                if (s0 + 16 * TP <= k_end) {
+                    load_step_full(s0, w, sw);
+                    return;
+                }
+            }
+            load_step(s0, w, sw);
+        };
+        load_any(k_begin, wc, sc);  // the first codes are in flight while the queries are prepared
 
         // ---- B operand: this lane's query channels (kb-major: LSPAN kb + 8 m + elem_channel(e);
         //      m-major: 32 m + 8 kb + elem_channel(e)) ----
@@ -396,7 +455,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
         };
 
         for (int s0 = k_begin; s0 < k_end; s0 += 16 * TP) {
-            if (s0 + 16 * TP < k_end) load_step(s0 + 16 * TP, wn, sn);
+            if (s0 + 16 * TP < k_end) load_any(s0 + 16 * TP, wn, sn);
 #pragma unroll
             for (int tt = 0; tt < TP; ++tt)
                 if (s0 + 16 * tt < k_end) tile(s0 + 16 * tt, wc[tt], sc[tt]);
@@ -431,6 +490,7 @@ hipError_t launch_d(const DecodeArgs& a, int group, hipStream_t st) {
 }  // namespace
 
 int64_t decode_chunks(int max_len) { return (max_len + kKeysPerWave - 1) / kKeysPerWave; }
+int decode_chunk_keys() { return kKeysPerWave; }
 
 hipError_t launch_decode_scores(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t st) {
     if (dtype == 1) {

@@ -90,6 +90,7 @@ hipError_t launch_stats(const StatsArgs& a, int n_blocks, int dtype, int head_di
 hipError_t launch_stats_final(const StatsFinalArgs& a, hipStream_t st);
 
 int64_t decode_chunks(int max_len);
+int decode_chunk_keys();  // keys per wave
 hipError_t launch_decode_scores(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t st);
 
 }  // namespace rrp

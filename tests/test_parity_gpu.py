@@ -650,3 +650,44 @@ def test_per_head_stats_and_sweep_parity(n, g):
             assert np.all(rel <= STAT_TOL), (b, got, r, rel)
             assert got[5] == r[5] and got[6] == r[6]
     print(f"workload {n} g={g} per head: rel_err by b", [round(float(np.sqrt(x[0] / x[1])), 5) for x in sw])
+
+
+def _bf16_bits_to_f32(a):
+    return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("layout,b", [(0, 8), (1, 64), (1, 2)])
+def test_per_head_fp32_inputs_and_layouts(layout, b):
+    """Per-key-head sets with fp32 rows (the bf16 workload's values widened) under
+    both RoPE pair layouts."""
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS[2], dtype="f32")
+    src = inputs(2)
+    T = 1024
+    sub = {"q": _bf16_bits_to_f32(src["q"][:T]), "k": _bf16_bits_to_f32(src["k"][:T]), "pos": src["pos"][:T],
+           "n_slots": T}
+    ang = random_angle_sets(w, 1400 + b)
+    out = run_rotate(w, sub, ang, b, 16, layout=layout, ah=w.n_kv_heads)
+    print(layout, b, check_rotate(w, sub, out, ang, b, 16, np.arange(T), layout=layout, ah=w.n_kv_heads))
+
+
+@pytest.mark.parametrize("ah,with_v", [(0, False), (0, True), (8, False)])
+def test_small_batch_split_matches_grid_stride_kernel(ah, with_v):
+    """Batches under 4096 tokens run the split-pass kernel family, larger ones the
+    grid-stride family: the same tokens give the same bits either way."""
+    w = W.WORKLOADS[3]
+    big = vinputs(3, 4096) if with_v else W.make_inputs(3, n_tokens=4096)
+    small = {k: (v[:4095] if isinstance(v, np.ndarray) else v) for k, v in big.items()}
+    small["n_slots"] = 4095
+    ang = random_angle_sets(w, 1500) if ah else random_angles(w.n_pairs, 1500)
+    run = (lambda inp: run_rotate_qkv(w, inp, ang, 128, 32, ah=ah)) if with_v else \
+        (lambda inp: run_rotate(w, inp, ang, 128, 32, ah=ah))
+    a, c = run(big), run(small)
+    keys = ["q_out", "codes", "scales", "q_rot_f32", "k_rot_f32", "k_scale_f32"]
+    if with_v:
+        keys += ["v_codes", "v_scales", "v_rot_f32", "v_scale_f32"]
+    for key in keys:
+        x, y = a[key][:4095], c[key]
+        if x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y), key

@@ -70,8 +70,19 @@ def cpu_baseline(w, inp, angles_np, budget_s=12.0):
     O.rotate_quantize_qk(shp, inp["q"][:n], inp["k"][:n], inp["pos"][:n], angles_np, 128, 128)
     dt = time.perf_counter() - t0
     threads = O.max_threads()
+    # the same oracle on one thread, over a smaller prefix (about 3 s)
+    n1 = int(min(w.n_tokens, max(64, 3.0 / max(per_tok * threads, 1e-9))))
+    prev = O.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        O.rotate_quantize_qk(shp, inp["q"][:n1], inp["k"][:n1], inp["pos"][:n1], angles_np, 128, 128)
+        dt1 = time.perf_counter() - t0
+    finally:
+        O.set_threads(prev)
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {w.n_tokens} tokens, same inputs and angles, {dt:.1f} s"}
+            "sample": f"first {n} of {w.n_tokens} tokens, same inputs and angles, {dt:.1f} s",
+            "single_thread": {"value": n1 / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"first {n1} tokens, {dt1:.1f} s"}}
 
 
 def to_device_bf16(a, dev):

@@ -71,6 +71,8 @@ def lib():
         L.orc_decode_scores.restype = ctypes.c_int
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = ctypes.c_int
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_set_threads.restype = ctypes.c_int
         for name in ("orc_rotate_quantize_qk", "orc_calibrate_moments",
                      "orc_angles_from_moments", "orc_quant_error_stats"):
             getattr(L, name).restype = ctypes.c_int
@@ -173,6 +175,11 @@ def pack_nibbles(q):
 def max_threads():
     """OpenMP threads the token-parallel oracle functions use."""
     return int(lib().orc_max_threads())
+
+
+def set_threads(n):
+    """Sets the OpenMP threads of later oracle calls; returns the previous count."""
+    return int(lib().orc_set_threads(int(n)))
 
 
 def shape(n_q_heads, n_kv_heads, head_dim, rope_theta, rope_layout=HALF_SPLIT, angle_heads=0):

@@ -581,3 +581,15 @@ int orc_max_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the threads later calls use (n >= 1); returns the previous count. */
+int orc_set_threads(int n)
+{
+    const int prev = orc_max_threads();
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return prev;
+}

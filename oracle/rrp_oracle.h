@@ -148,6 +148,7 @@ int orc_decode_scores(const orc_shape* s, int dtype, const void* q, int64_t n_se
 
 /* Threads the token-parallel entry points may use (OpenMP), 1 without OpenMP. */
 int orc_max_threads(void);
+int orc_set_threads(int n);
 
 #ifdef __cplusplus
 }

@@ -241,8 +241,8 @@ def main():
     ap.add_argument("--hot-path-only", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported here (the path shards "
-              "over tokens or heads without communication, but no multi-GPU run is part of this build)",
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards over "
+              "tokens or heads with no communication; only the one-GPU throughput is measured)",
               file=sys.stderr)
         sys.exit(2)
 

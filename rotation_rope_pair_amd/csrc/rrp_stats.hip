@@ -280,8 +280,8 @@ template <int D> struct Log2;
 template <> struct Log2<64> { static constexpr int value = 6; };
 template <> struct Log2<128> { static constexpr int value = 7; };
 
-// Supports 2^J0 .. 2^(J1-1) of the sweep (the sweep runs as two launches, so
-// each keeps half the per-support sums in registers).
+// Supports 2^J0 .. 2^(J1-1) of the sweep (the sweep runs as several launches,
+// each keeping its supports' sums in registers).
 template <typename E, int D, int LAYOUT, bool SMALLG, int J0, int J1, bool PH>
 __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
     using G = Geo<E, D>;
@@ -394,19 +394,31 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const StatsFinalArgs a
     }
 }
 
+// The sweep's supports are split over kSweepParts launches (each keeps its
+// supports' sums in registers and reads K once).
+#ifndef RRP_SWEEP_PARTS
+#define RRP_SWEEP_PARTS 4
+#endif
+constexpr int kSweepParts = RRP_SWEEP_PARTS;
+
+template <typename E, int D, int LAYOUT, bool SG, bool PH, int J0, int NB, int W>
+void launch_sweep_parts(const StatsArgs& a, int n_blocks, hipStream_t st) {
+    if constexpr (J0 < NB) {
+        constexpr int J1 = J0 + W < NB ? J0 + W : NB;
+        hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, SG, J0, J1, PH>), dim3(n_blocks), dim3(256), 0, st, a);
+        launch_sweep_parts<E, D, LAYOUT, SG, PH, J1, NB, W>(a, n_blocks, st);
+    }
+}
+
 template <typename E, int D, int LAYOUT, bool PH>
 hipError_t launch_p(const StatsArgs& a, int n_blocks, bool sweep, hipStream_t st) {
     constexpr int CE = Geo<E, D>::CE;
     const bool small = a.group < CE;
     if (sweep) {
-        constexpr int NB = Log2<D>::value + 1, JH = NB / 2;
-        if (small) {
-            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, true, 0, JH, PH>), dim3(n_blocks), dim3(256), 0, st, a);
-            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, true, JH, NB, PH>), dim3(n_blocks), dim3(256), 0, st, a);
-        } else {
-            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, false, 0, JH, PH>), dim3(n_blocks), dim3(256), 0, st, a);
-            hipLaunchKernelGGL((stats_sweep_kernel<E, D, LAYOUT, false, JH, NB, PH>), dim3(n_blocks), dim3(256), 0, st, a);
-        }
+        constexpr int NB = Log2<D>::value + 1;
+        constexpr int W = (NB + kSweepParts - 1) / kSweepParts;  // supports per launch
+        if (small) launch_sweep_parts<E, D, LAYOUT, true, PH, 0, NB, W>(a, n_blocks, st);
+        else launch_sweep_parts<E, D, LAYOUT, false, PH, 0, NB, W>(a, n_blocks, st);
         return hipGetLastError();
     }
 #define RRP_LAUNCH(BT, SG) \

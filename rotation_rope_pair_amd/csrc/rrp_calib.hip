@@ -290,7 +290,7 @@ int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, in
     // about RRP_CALIB_TABLE_WEIGHT passes).
     int64_t want = (n_tokens * (with_q ? 2 : 1) + 31) / 32;
     if (want > kMaxCalibBlocks) want = kMaxCalibBlocks;
-    want = (want + n_sets - 1) / n_sets;  // per set
+    want /= n_sets;  // per set (so all sets together stay within kMaxCalibBlocks)
     if (want < (with_q ? 2 : 1)) want = with_q ? 2 : 1;
     const int total = (int)want;
     if (!with_q || hq == 0) {

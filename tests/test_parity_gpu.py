@@ -691,3 +691,15 @@ def test_small_batch_split_matches_grid_stride_kernel(ah, with_v):
         if x.dtype == torch.bfloat16:
             x, y = x.view(torch.int16), y.view(torch.int16)
         assert torch.equal(x, y), key
+
+
+def test_per_head_in_place_and_k_only():
+    """Per-key-head sets with Q rotated in place, and with no Q at all."""
+    w, inp = W.WORKLOADS[2], inputs(2)
+    hk = w.n_kv_heads
+    ang = random_angle_sets(w, 1600)
+    out = run_rotate(w, inp, ang, 32, 64, in_place=True, ah=hk)
+    check_rotate(w, inp, out, ang, 32, 64, np.arange(w.n_tokens), ah=hk)
+    out2 = run_rotate(w, inp, ang, 32, 64, with_q=False, ah=hk)
+    check_rotate(w, inp, out2, ang, 32, 64, np.arange(w.n_tokens), with_q=False, ah=hk)
+    assert torch.equal(out["codes"], out2["codes"]) and torch.equal(out["scales"], out2["scales"])

@@ -453,9 +453,9 @@ def test_calibration_is_deterministic():
 STAT_TOL = np.array([1e-9, 1e-11, 1e-11, 1e-13, 1e-11])
 
 
-def run_stats(w, k, pos, angles, b, g, ah=0):
+def run_stats(w, k, pos, angles, b, g, ah=0, layout=0):
     st = torch.empty(8, dtype=torch.float64, device=DEV)
-    rrp.quant_error_stats(shape_of(w, 0, ah), to_dev(k), to_dev(pos), support_b=b, group=g, stats_out=st,
+    rrp.quant_error_stats(shape_of(w, layout, ah), to_dev(k), to_dev(pos), support_b=b, group=g, stats_out=st,
                           angles=None if angles is None else to_dev(angles))
     torch.cuda.synchronize()
     return st.cpu().numpy()
@@ -486,10 +486,10 @@ def test_quant_error_stats_is_deterministic():
     assert np.array_equal(a, b)
 
 
-def run_sweep(w, k, pos, angles, g, ah=0):
+def run_sweep(w, k, pos, angles, g, ah=0, layout=0):
     nb = len(rrp.sweep_supports(w.head_dim))
     st = torch.empty((nb, 8), dtype=torch.float64, device=DEV)
-    rrp.quant_error_sweep(shape_of(w, 0, ah), to_dev(k), to_dev(pos), group=g, stats_out=st,
+    rrp.quant_error_sweep(shape_of(w, layout, ah), to_dev(k), to_dev(pos), group=g, stats_out=st,
                           angles=None if angles is None else to_dev(angles))
     torch.cuda.synchronize()
     return st.cpu().numpy()
@@ -703,3 +703,35 @@ def test_per_head_in_place_and_k_only():
     out2 = run_rotate(w, inp, ang, 32, 64, with_q=False, ah=hk)
     check_rotate(w, inp, out2, ang, 32, 64, np.arange(w.n_tokens), with_q=False, ah=hk)
     assert torch.equal(out["codes"], out2["codes"]) and torch.equal(out["scales"], out2["scales"])
+
+
+@pytest.mark.parametrize("n,est,ah", [(1, "default", 0), (2, "default", 0), (2, "stream_balanced", 0),
+                                      (2, "default", 8), (3, "k_only", 8)])
+def test_calibration_parity_interleaved_pairs(n, est, ah):
+    """Calibration with the interleaved RoPE pair layout (pairs (2k, 2k + 1))."""
+    w = W.WORKLOADS[n]
+    T = min(w.n_tokens, 2048)
+    inp = W.make_inputs(n, n_tokens=T)
+    q = inp["q"] if est != "k_only" else None
+    mom_g, ang_g = run_calib(w, q, inp["k"], inp["pos"], est, layout=1, ah=ah)
+    mom_r = O.calibrate_moments(oshape_of(w, 1, ah=ah), q, inp["k"], inp["pos"])
+    phi64, _, abc = O.angles_from_moments(mom_r, EST[est])
+    worst = C.compare_moments(mom_g, mom_r)
+    rep = C.compare_angles(ang_g.reshape(-1), phi64.reshape(-1), abc.reshape(-1, 3))
+    print(f"workload {n} {est} sets={max(ah, 1)} interleaved: moments {worst:.2e} {rep}")
+
+
+@pytest.mark.parametrize("n,g,ah", [(1, 64, 0), (2, 8, 0), (3, 128, 8)])
+def test_stats_and_sweep_parity_interleaved_pairs(n, g, ah):
+    w = W.WORKLOADS[n]
+    T = min(w.n_tokens, 512)
+    inp = W.make_inputs(n, n_tokens=T)
+    ang = random_angle_sets(w, 1700 + n) if ah else random_angles(w.n_pairs, 1700 + n)
+    sw = run_sweep(w, inp["k"], inp["pos"], ang, g, ah=ah, layout=1)
+    for j, b in enumerate(rrp.sweep_supports(w.head_dim)):
+        r = O.quant_error_stats(oshape_of(w, 1, ah=ah), inp["k"], inp["pos"], ang, b, g)
+        one = run_stats(w, inp["k"], inp["pos"], ang, b, g, ah=ah, layout=1)
+        for got in (sw[j], one):
+            rel = np.abs(got[:5] - r[:5]) / np.maximum(np.abs(r[:5]), 1e-300)
+            assert np.all(rel <= STAT_TOL), (b, got, r, rel)
+            assert got[5] == r[5] and got[6] == r[6]

@@ -12,6 +12,8 @@
 // partials go to a scratch array laid out [pair * 5 + sum][block], which one
 // wave per (stream, pair, sum) reduces in a fixed order -- so the moments are
 // bit-identical from run to run.
+#include <type_traits>
+
 #include "rrp_device.hpp"
 #include "rrp_kernels.hpp"
 
@@ -196,6 +198,168 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
     }
 }
 
+// Per-key-head angle sets.  A block's kSetWaves waves take kSetWaves sets of one
+// stream (wave w: set sg * kSetWaves + w) and walk the same groups of
+// kSetWaves tokens: wave j builds the RoPE table of the group's token j into
+// LDS, so each token's table is built once per block instead of once per set,
+// and each wave then reads the rows (token j, head h) of its own set, flattened
+// over the group and cut into passes of RP rows.  A set with one head per
+// stream (the K stream) thus still fills every row group of a pass.  Each wave
+// writes its set's partials to column set * (nbq + nbk) + (block's place in the
+// set-group run), the layout calib_reduce_kernel reads.
+constexpr int kSetWaves = 4;
+
+template <typename E, int D, int LAYOUT, int MAXP>
+__global__ __launch_bounds__(64 * kSetWaves)
+__attribute__((amdgpu_waves_per_eu(std::is_same<E, bf16_tag>::value ? 4 : 1)))  // bf16 fits 128 VGPRs
+void calib_sets_kernel(const CalibArgs a) {
+    constexpr int P = D / 2;
+    constexpr int LP = P / kCP;  // lanes per row
+    constexpr int RP = 64 / LP;  // rows per pass
+    constexpr int EB = ElemInfo<E>::bytes;
+    constexpr size_t ROWB = (size_t)D * EB;
+    using QT = typename Quad<E>::T;
+    __shared__ double2 tab[kSetWaves][P];
+
+    const int lane = (int)__lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int s = lane % LP;
+    const int grp = lane / LP;
+
+    // Neighbouring blocks take the same tokens for different set-groups, so the
+    // rows of a token (every head) are read at about the same time.
+    const int per_set = a.nbq + a.nbk;
+    const int n_sg = (a.n_sets + kSetWaves - 1) / kSetWaves;
+    const int sg = (int)blockIdx.x % n_sg;
+    const int local = (int)blockIdx.x / n_sg;
+    const bool is_k = local >= a.nbq;
+    const int bs = is_k ? local - a.nbq : local;
+    const int nb = is_k ? a.nbk : a.nbq;
+    const int set = sg * kSetWaves + wave;
+    const bool active = set < a.n_sets;  // waves past the last set still build tables
+    const unsigned char* src = static_cast<const unsigned char*>(is_k ? a.k : a.q);
+    const int nh_all = is_k ? a.hk : a.hq;
+    const int g = nh_all / a.n_sets;  // heads per set
+    const int h0 = set * g;
+    const int nrows = kSetWaves * g;  // rows per token group
+    const int npass = (nrows + RP - 1) / RP;
+    const int nstep = (npass + MAXP - 1) / MAXP;
+    const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
+    const int off0 = LAYOUT == 0 ? s * kCP : 2 * s * kCP;
+    const int off1 = LAYOUT == 0 ? P + s * kCP : 2 * s * kCP + kCP;
+
+    double acc[kCP][kNSum];
+#pragma unroll
+    for (int j = 0; j < kCP; ++j)
+#pragma unroll
+        for (int m = 0; m < kNSum; ++m) acc[j][m] = 0.0;
+
+    // Token groups bs, bs + nb, ...: tokens kSetWaves * group + j.
+    const int64_t n_groups = (a.n_tokens + kSetWaves - 1) / kSetWaves;
+    auto row_valid = [&](int64_t grp_t, int r, int64_t& t, int& h) {
+        const int j = r / g;
+        t = grp_t * kSetWaves + j;
+        h = h0 + (r - j * g);
+        return active && r < nrows && t < a.n_tokens;
+    };
+    auto load_step = [&](int64_t grp_t, int st, QT (&raw)[MAXP][2]) {
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            const int pass = st * MAXP + i;
+            int64_t t;
+            int h;
+            if (pass < npass && row_valid(grp_t, pass * RP + grp, t, h)) {
+                const unsigned char* rp = src + ((size_t)t * nh_all + h) * ROWB;
+                raw[i][0] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(rp + off0 * EB));
+                raw[i][1] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(rp + off1 * EB));
+            } else {
+                raw[i][0] = raw[i][1] = Quad<E>::zero();
+            }
+        }
+    };
+
+    int64_t gt = bs;
+    int st = 0;
+    QT cur[MAXP][2], nxt[MAXP][2];
+    if (gt < n_groups) load_step(gt, 0, cur);
+    while (gt < n_groups) {
+        int64_t gn = gt;
+        int sn_step = st + 1;
+        if (sn_step == nstep) {
+            gn = gt + nb;
+            sn_step = 0;
+        }
+        if (gn < n_groups) load_step(gn, sn_step, nxt);
+        if (st == 0) {
+            __syncthreads();  // the previous group's table reads are complete
+            const int64_t t = gt * kSetWaves + wave;
+            if (lane < P && t < a.n_tokens) {
+                double sa, ca;
+                sincos_f64_of_f32(rope_angle_f32(a.pos[t], invf), sa, ca);
+                tab[wave][lane] = make_double2(ca, sa);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            const int pass = st * MAXP + i;
+            int64_t t;
+            int h;
+            if (!(pass < npass && row_valid(gt, pass * RP + grp, t, h))) continue;
+            const int j = (pass * RP + grp) / g;  // token of the row inside the group
+            float x0[4], x1[4];
+            Quad<E>::unpack(cur[i][0], x0);
+            Quad<E>::unpack(cur[i][1], x1);
+#pragma unroll
+            for (int q = 0; q < kCP; ++q) {
+                const double2 cs = tab[j][s * kCP + q];
+                double xa, xb;
+                if constexpr (LAYOUT == 0) {
+                    xa = x0[q];
+                    xb = x1[q];
+                } else if (q < kCP / 2) {
+                    xa = x0[2 * q];
+                    xb = x0[2 * q + 1];
+                } else {
+                    xa = x1[2 * (q - kCP / 2)];
+                    xb = x1[2 * (q - kCP / 2) + 1];
+                }
+                const double u = xa * cs.x - xb * cs.y;
+                const double v = xb * cs.x + xa * cs.y;
+                acc[q][0] += u;
+                acc[q][1] += v;
+                acc[q][2] += u * u;
+                acc[q][3] += v * v;
+                acc[q][4] += u * v;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            cur[i][0] = nxt[i][0];
+            cur[i][1] = nxt[i][1];
+        }
+        gt = gn;
+        st = sn_step;
+    }
+
+    // Fold the wave's row groups in a fixed order; the row-group-0 lanes write
+    // their four pairs' sums to this set's column.
+#pragma unroll
+    for (int m = LP; m < 64; m <<= 1)
+#pragma unroll
+        for (int j = 0; j < kCP; ++j)
+#pragma unroll
+            for (int q = 0; q < kNSum; ++q) acc[j][q] += shfl_xor_d(acc[j][q], m);
+    if (active && grp == 0) {
+        const int nbt = per_set * a.n_sets;
+        const size_t col = (size_t)set * per_set + local;
+#pragma unroll
+        for (int j = 0; j < kCP; ++j)
+#pragma unroll
+            for (int q = 0; q < kNSum; ++q) a.partials[(size_t)((s * kCP + j) * kNSum + q) * nbt + col] = acc[j][q];
+    }
+}
+
 // One wave per (set, stream, pair, sum): lane l adds the partials of the set's
 // stream blocks l, l + 64, ... in order, then the wave folds its lanes with a
 // fixed xor butterfly (every lane ends with the same value), and lane 0 adds it
@@ -272,7 +436,14 @@ __global__ __launch_bounds__(512) void calib_angles_kernel(const CalibFinalArgs 
 
 template <typename E, int D, int LAYOUT>
 hipError_t launch_t(const CalibArgs& a, hipStream_t st) {
-    const int blocks = (a.nbq + a.nbk) * a.n_sets;
+    if (a.n_sets > 1) {
+        const int groups = (a.n_sets + kSetWaves - 1) / kSetWaves;
+        const int blocks = (a.nbq + a.nbk) * groups;
+        hipLaunchKernelGGL((calib_sets_kernel<E, D, LAYOUT, RRP_CALIB_MAXP>), dim3(blocks), dim3(64 * kSetWaves), 0,
+                           st, a);
+        return hipGetLastError();
+    }
+    const int blocks = a.nbq + a.nbk;
     hipLaunchKernelGGL((calib_moments_kernel<E, D, LAYOUT, RRP_CALIB_MAXP>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -284,10 +455,10 @@ hipError_t launch_t(const CalibArgs& a, hipStream_t st) {
 #endif
 
 int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, int n_sets, int* nbq, int* nbk) {
-    // About 8 tokens per wave per stream, at most kMaxCalibBlocks blocks over all
-    // sets.  The streams share a set's blocks in proportion to their work per
-    // token: the row passes of the set's heads plus the token's table (worth
-    // about RRP_CALIB_TABLE_WEIGHT passes).
+    // About 8 tokens per wave per stream, at most kMaxCalibBlocks partial columns
+    // over all sets.  The streams share a set's blocks in proportion to their
+    // work per token (per token group for per-set calibration): the row passes
+    // plus the table (worth about RRP_CALIB_TABLE_WEIGHT passes).
     int64_t want = (n_tokens * (with_q ? 2 : 1) + 31) / 32;
     if (want > kMaxCalibBlocks) want = kMaxCalibBlocks;
     want /= n_sets;  // per set (so all sets together stay within kMaxCalibBlocks)
@@ -297,9 +468,11 @@ int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, in
         *nbq = 0;
         *nbk = total;
     } else {
+        // rows per token (one shared set) or per group of kSetWaves tokens (per-set kernel)
         const int rp = 512 / head_dim;  // rows per pass
-        const int64_t wq = (hq / n_sets + rp - 1) / rp + RRP_CALIB_TABLE_WEIGHT;
-        const int64_t wk = (hk / n_sets + rp - 1) / rp + RRP_CALIB_TABLE_WEIGHT;
+        const int tg = n_sets > 1 ? kSetWaves : 1;
+        const int64_t wq = (tg * (hq / n_sets) + rp - 1) / rp + RRP_CALIB_TABLE_WEIGHT;
+        const int64_t wk = (tg * (hk / n_sets) + rp - 1) / rp + RRP_CALIB_TABLE_WEIGHT;
         int q = (int)((int64_t)total * wq / (wq + wk));
         if (q < 1) q = 1;
         if (q > total - 1) q = total - 1;

@@ -1,17 +1,18 @@
 // rrp_calib.hip -- calibration pass: fp64 post-RoPE pair moments pooled over
 // heads and tokens, then the closed-form minimax-variance angle per pair.
 //
-// Per angle set (one shared set, or one per key head), blocks [0, nbq) of the
-// set's run accumulate the Q stream of its heads, blocks [nbq, nbq + nbk) the
-// K stream.  A row of head_dim channels is held by P/4 lanes, each with four
+// One angle set shared by all heads (calib_moments_kernel): blocks [0, nbq)
+// accumulate the Q stream, blocks [nbq, nbq + nbk) the K stream.  One set per
+// key head: calib_sets_kernel below.  A row of head_dim channels is held by P/4
+// lanes, each with four
 // RoPE pairs (two 8-byte loads for bf16, two 16-byte loads for fp32), so the
 // five fp64 sums per pair stay within a few dozen registers.  Each wave walks
 // tokens with a fixed stride and keeps the next group of row passes in flight
 // while it accumulates the current one.  A wave's row groups are folded with
 // lane shuffles, the block's waves through LDS, both in a fixed order; block
-// partials go to a scratch array laid out [pair * 5 + sum][block], which one
-// wave per (stream, pair, sum) reduces in a fixed order -- so the moments are
-// bit-identical from run to run.
+// partials go to a scratch array laid out [pair * 5 + sum][column], which one
+// wave per (set, stream, pair, sum) reduces in a fixed order -- so the moments
+// are bit-identical from run to run.
 #include <type_traits>
 
 #include "rrp_device.hpp"

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
     const int h0 = set * nh;
     const int npass = (nh + RP - 1) / RP;
     const int nstep = (npass + MAXP - 1) / MAXP;
-    const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
+    const float invf = lane_inv_freq(a.inv_freq, lane, P);
     // Element offsets of the lane's two quads: half-split pairs (k, k + P) for
     // k in [4s, 4s + 4); interleaved pairs (2k, 2k + 1) for the same k.
     const int off0 = LAYOUT == 0 ? s * kCP : 2 * s * kCP;
@@ -114,6 +114,11 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
     int st = 0;
     QT cur[MAXP][2], nxt[MAXP][2];
     if (t < a.n_tokens) load_step(t, 0, cur);
+    // Retire the first step here: inside the loop `cur` is then always a copy
+    // made after its wait, and the loop's first use of it needs no wait (which
+    // would otherwise also take the next step's prefetch on every iteration).
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) asm volatile("" ::"v"(cur[i][0]), "v"(cur[i][1]));
     double c[kCP], sn[kCP];
     while (t < a.n_tokens) {
         int64_t tn = t;
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
         }
         if (tn < a.n_tokens) load_step(tn, sn_step, nxt);
         if (st == 0) {
-            const int p = a.pos[t];
+            const int p = token_pos(a.pos, t);
             wave_lds_sync();  // previous token's table reads are complete
             if (lane < P) {
                 double sa, ca;
@@ -245,7 +250,7 @@ void calib_sets_kernel(const CalibArgs a) {
     const int nrows = kSetWaves * g;  // rows per token group
     const int npass = (nrows + RP - 1) / RP;
     const int nstep = (npass + MAXP - 1) / MAXP;
-    const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
+    const float invf = lane_inv_freq(a.inv_freq, lane, P);
     const int off0 = LAYOUT == 0 ? s * kCP : 2 * s * kCP;
     const int off1 = LAYOUT == 0 ? P + s * kCP : 2 * s * kCP + kCP;
 
@@ -283,6 +288,11 @@ void calib_sets_kernel(const CalibArgs a) {
     int st = 0;
     QT cur[MAXP][2], nxt[MAXP][2];
     if (gt < n_groups) load_step(gt, 0, cur);
+    // Retire the first step here: inside the loop `cur` is then always a copy
+    // made after its wait, and the loop's first use of it needs no wait (which
+    // would otherwise also take the next step's prefetch on every iteration).
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) asm volatile("" ::"v"(cur[i][0]), "v"(cur[i][1]));
     while (gt < n_groups) {
         int64_t gn = gt;
         int sn_step = st + 1;
@@ -296,7 +306,7 @@ void calib_sets_kernel(const CalibArgs a) {
             const int64_t t = gt * kSetWaves + wave;
             if (lane < P && t < a.n_tokens) {
                 double sa, ca;
-                sincos_f64_of_f32(rope_angle_f32(a.pos[t], invf), sa, ca);
+                sincos_f64_of_f32(rope_angle_f32(token_pos(a.pos, t), invf), sa, ca);
                 tab[wave][lane] = make_double2(ca, sa);
             }
             __syncthreads();

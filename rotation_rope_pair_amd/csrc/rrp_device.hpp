@@ -167,6 +167,23 @@ __device__ __forceinline__ int chunk_offset(int ch, int s) {
 // Angles.
 // ---------------------------------------------------------------------------
 
+// The lane's RoPE frequency from the kernel argument block; the empty asm uses
+// it at once, so its load is waited for here, before the token loop.  Waited
+// for at its first use inside the loop instead, the wait cannot be told apart
+// from the loop's own loads and takes all of them, the next token's prefetched
+// rows included, on every token.
+__device__ __forceinline__ float lane_inv_freq(const float* inv_freq, int lane, int n_pairs) {
+    const float f = lane < n_pairs ? inv_freq[lane] : 0.0f;
+    asm volatile("" ::"v"(f));
+    return f;
+}
+
+// A token's position, read through the scalar unit (read-only input): its
+// wait is then separate from the wave's row loads.
+__device__ __forceinline__ int token_pos(const int32_t* pos, int64_t t) {
+    return ((const __attribute__((address_space(4))) int32_t*)pos)[t];
+}
+
 // RoPE angle of one pair at position p: a single fp32 product, never fused.
 __device__ __forceinline__ float rope_angle_f32(int p, float w) {
 #pragma clang fp contract(off)

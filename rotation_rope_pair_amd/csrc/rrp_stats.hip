@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     double cphi = 1.0, sphi = 0.0;
     if constexpr (PH) load_angle_sets<P>(phi_all, a.angles, a.angle_sets);
     else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
-    const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
+    const float invf = lane_inv_freq(a.inv_freq, lane, P);
     const int s_src = s ^ lane_perm_mask<D, CE>(BT ? BT : a.support_b);  // permuted loads, see fwht_row
     int kidx[CE];
     pair_index_of_lane<D, LAYOUT, CE>(s_src, kidx);
@@ -180,6 +180,10 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     int ps = 0;
     u32x4 cur[2], nxt[2];
     if (t < a.n_tokens) load_pass(t, 0, cur);
+    // Retire the first pass here: inside the loop `cur` is then always a copy
+    // made after its wait, and the loop's first use of it needs no wait (which
+    // would otherwise also take the next pass's prefetch on every iteration).
+    asm volatile("" ::"v"(cur[0]), "v"(cur[1]));
     while (t < a.n_tokens) {
         // keep the next pass (this token's or the next token's first) in flight
         int64_t tn = t;
@@ -190,8 +194,8 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
         }
         if (tn < a.n_tokens) load_pass(tn, pn, nxt);
         if (ps == 0) {
-            if constexpr (PH) token_tables_sets<D, FOLD>(nullptr, tab64, lane, a.pos[t], invf, phi_all, a.angle_sets, a.rsqrt_b);
-            else token_tables<D, FOLD>(tab32, tab64, lane, a.pos[t], invf, cphi, sphi, a.rsqrt_b);
+            if constexpr (PH) token_tables_sets<D, FOLD>(nullptr, tab64, lane, token_pos(a.pos, t), invf, phi_all, a.angle_sets, a.rsqrt_b);
+            else token_tables<D, FOLD>(tab32, tab64, lane, token_pos(a.pos, t), invf, cphi, sphi, a.rsqrt_b);
         }
         if (ps * R + grp < a.hk) {
             float yf[2][CE];
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
     double cphi = 1.0, sphi = 0.0;
     if constexpr (PH) load_angle_sets<P>(phi_all, a.angles, a.angle_sets);
     else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
-    const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
+    const float invf = lane_inv_freq(a.inv_freq, lane, P);
     int kidx[CE];
     pair_index_of_lane<D, LAYOUT, CE>(s, kidx);  // natural chunk order
     if constexpr (PH) {
@@ -335,6 +339,10 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
     int ps = 0;
     u32x4 cur[2], nxt[2];
     if (t < a.n_tokens) load_pass(t, 0, cur);
+    // Retire the first pass here: inside the loop `cur` is then always a copy
+    // made after its wait, and the loop's first use of it needs no wait (which
+    // would otherwise also take the next pass's prefetch on every iteration).
+    asm volatile("" ::"v"(cur[0]), "v"(cur[1]));
     while (t < a.n_tokens) {
         int64_t tn = t;
         int pn = ps + 1;
@@ -344,8 +352,8 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
         }
         if (tn < a.n_tokens) load_pass(tn, pn, nxt);
         if (ps == 0) {
-            if constexpr (PH) token_tables_sets<D, false>(nullptr, tab64, lane, a.pos[t], invf, phi_all, a.angle_sets, 1.0);
-            else token_tables<D, false>(tab32, tab64, lane, a.pos[t], invf, cphi, sphi, 1.0);
+            if constexpr (PH) token_tables_sets<D, false>(nullptr, tab64, lane, token_pos(a.pos, t), invf, phi_all, a.angle_sets, 1.0);
+            else token_tables<D, false>(tab32, tab64, lane, token_pos(a.pos, t), invf, cphi, sphi, 1.0);
         }
         if (ps * R + grp < a.hk) {
             float yf[2][CE];

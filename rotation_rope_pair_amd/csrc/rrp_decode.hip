@@ -454,6 +454,19 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
             }
         };
 
+        // Retire the first step's loads here (the queries were prepared while they
+        // were in flight): inside the loop the current step is then always a copy
+        // made after its wait, and its first use needs no wait, which would
+        // otherwise also take part of the next step's prefetch on every step.
+#pragma unroll
+        for (int tt = 0; tt < TP; ++tt) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) asm volatile("" ::"v"(wc[tt][m]));
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int x = 0; x < NSW; ++x) asm volatile("" ::"v"(sc[tt][r][x]));
+        }
         for (int s0 = k_begin; s0 < k_end; s0 += 16 * TP) {
             if (s0 + 16 * TP < k_end) load_any(s0 + 16 * TP, wn, sn);
 #pragma unroll

@@ -229,7 +229,9 @@ int rrp_quant_error_sweep(const rrp_shape* shape, int32_t dtype, const void* k, 
  * of exact f16 products on the matrix cores).
  *
  * shape       host; n_q_heads a multiple of n_kv_heads, at most 16 query heads
- *             per key head (else RRP_ERR_UNSUPPORTED); head_dim 64 or 128.
+ *             per key head, and 256 * n_kv_heads * head_dim/2 < 2^31 (a slot row
+ *             band of 256 keys addressed by 32-bit offsets; else
+ *             RRP_ERR_UNSUPPORTED); head_dim 64 or 128.
  * dtype       dtype of q: RRP_BF16 or RRP_F32.
  * q           [n_seqs][n_q_heads][head_dim] rotated queries (the q_out of
  *             rrp_rotate_quantize_qk for the decode tokens), 16-byte aligned.

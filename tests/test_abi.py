@@ -121,6 +121,7 @@ def test_decode_scores_validation(lib):
     assert dec(shape=_shape(hq=12, hk=8)) == 1                    # query heads not a multiple of key heads
     assert dec(shape=_shape(hq=0)) == 1
     assert dec(shape=_shape(hq=32, hk=1)) == 3                    # more than 16 query heads per key head
+    assert dec(shape=_shape(hq=1 << 17, hk=1 << 17)) == 3         # a 256-key band past 32-bit offsets
     assert dec(g=3) == 1 and dec(g=256) == 1 and dec(g=1) == 1
     assert dec(B=-1) == 1 and dec(n_slots=-1) == 1 and dec(max_len=-5) == 1 and dec(n_slots=0) == 1
     assert dec(q=None) == 1 and dec(codes=None) == 1 and dec(scales=None) == 1

@@ -10,13 +10,14 @@
 // that share the key head (f16, each head scaled by a power of two so that its
 // largest value sits just below 2^15; fp32 queries as a hi + lo pair of f16
 // terms).  Products of f16 values are exact in the fp32 accumulator.  Each MFMA
-// covers 32 consecutive channels; the group scales (fp16 -> fp32) multiply the
-// per-group partial sums in fp32, so the codes never meet a rounded scale.
+// contracts 32 channels, arranged so that the per-group partial sums can be
+// kept apart (see KBM and SWAP in the kernel); the group scales (fp16 -> fp32)
+// multiply those partial sums in fp32, so the codes never meet a rounded scale.
 //
 // Lane roles (16x16x32 layout): A row i = lane % 16 (key), k block kb = lane / 16
 // (8 channels per MFMA); B column j = lane % 16 (query head); D holds keys
 // 4 * (lane / 16) + r, r = 0..3, of column lane % 16.  Which channels an MFMA
-// contracts is a free choice as long as A and B agree (see KBM in the kernel).
+// contracts is a free choice as long as A and B agree (see KBM and SWAP).
 // Inside a lane's 8 channels the element order is (0, 4, 1, 5, 2, 6, 3, 7): that
 // is the order in which the nibble-to-f16 conversion produces them, and B is laid
 // out the same way.
@@ -132,6 +133,12 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
     // ("m-major"): MFMA m takes the 32 consecutive channels [32 m, 32 m + 32),
     // lane block kb the 8 at 32 m + 8 kb.
     constexpr bool KBM = GS >= D / 4;
+    // Two groups per row (kb-major): lane blocks 0-1 hold group 0, 2-3 group 1.
+    // Swapping the upper half-wave of word 2i with the lower half-wave of word
+    // 2i + 1 (v_permlane32_swap) turns each pair of words into one operand of
+    // each group, so every MFMA stays inside one group and the query operand
+    // needs no per-group masked copies.
+    constexpr bool SWAP = KBM && NG == 2;
     constexpr int LSPAN = D / 4;                // channels per lane block (kb-major)
     constexpr int KPG = KBM ? GS / LSPAN : 1;   // lane blocks per group (kb-major)
 
@@ -329,7 +336,16 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
             if (head_ok) {
                 const void* row = static_cast<const unsigned char*>(a.q) +
                                   ((size_t)b * a.hq + h) * D * ElemInfo<E>::bytes;
-                QLoad<E>::load(row, KBM ? LSPAN * kb + 8 * m : 32 * m + 8 * kb, x);
+                int c0;
+                if constexpr (SWAP) {
+                    // operand m = 2i (group 0) / 2i + 1 (group 1) after the half-wave swap
+                    const int i = m >> 1;
+                    if ((m & 1) == 0) c0 = kb < 2 ? LSPAN * kb + 16 * i : LSPAN * (kb - 2) + 16 * i + 8;
+                    else c0 = kb < 2 ? LSPAN * (kb + 2) + 16 * i : LSPAN * kb + 16 * i + 8;
+                } else {
+                    c0 = KBM ? LSPAN * kb + 8 * m : 32 * m + 8 * kb;
+                }
+                QLoad<E>::load(row, c0, x);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = 0.0f;
@@ -355,29 +371,39 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
             }
         float* out_row = a.scores + ((size_t)b * a.hq + h) * a.max_len;
         const float descale = ldexpf(1.0f, -qexp);
-        // kb-major with two groups: the query operand masked to each group's lane blocks
-        constexpr int NGM = (KBM && NG == 2) ? 2 : 1;
-        half8 bqg[NGM][SPLIT][NM];
-        if constexpr (NGM == 2) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int t = 0; t < SPLIT; ++t)
-#pragma unroll
-                    for (int m = 0; m < NM; ++m)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            bqg[q][t][m][e] = (kb / KPG == q) ? bq[t][m][e] : (_Float16)0.0f;
-        }
-
         // One 16-key tile: dequantise, contract on the matrix cores, scale, store.
         auto tile = [&](int key0, const unsigned (&w)[NM], const unsigned (&sw)[4][NSW]) {
             half8 am[NM];
+            if constexpr (SWAP) {
+                // words 2i, 2i + 1 -> one operand of group 0 and one of group 1
 #pragma unroll
-            for (int m = 0; m < NM; ++m) am[m] = codes_to_half8(w[m]);
+                for (int i = 0; i < NM / 2; ++i) {
+                    const auto xy = __builtin_amdgcn_permlane32_swap(w[2 * i], w[2 * i + 1], false, false);
+                    am[2 * i] = codes_to_half8(xy[0]);
+                    am[2 * i + 1] = codes_to_half8(xy[1]);
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < NM; ++m) am[m] = codes_to_half8(w[m]);
+            }
 
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            if constexpr (KBM) {
+            if constexpr (SWAP) {
+#pragma unroll
+                for (int gq = 0; gq < 2; ++gq) {
+                    f32x4 dq = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int m = gq; m < NM; m += 2)
+#pragma unroll
+                        for (int t = 0; t < SPLIT; ++t)
+                            dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(am[m], bq[t][m], dq, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float scl = f16_bits_to_f32((unsigned short)(sw[r][0] >> (16 * gq)));
+                        acc[r] = fmaf(scl, dq[r], acc[r]);
+                    }
+                }
+            } else if constexpr (KBM) {
 #pragma unroll
                 for (int gq = 0; gq < NG; ++gq) {
                     f32x4 dq = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -387,7 +413,6 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
                         for (int t = 0; t < SPLIT; ++t) {
                             half8 bm;
                             if constexpr (NG == 1) bm = bq[t][m];
-                            else if constexpr (NGM == 2) bm = bqg[gq][t][m];
                             else bm = (kb / KPG == gq) ? bq[t][m] : half8{};
                             dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(am[m], bm, dq, 0, 0, 0);
                         }

@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
                     sw[r][0] = *reinterpret_cast<const unsigned short*>(row);
                 } else if constexpr (SROW == 4) {
                     sw[r][0] = *reinterpret_cast<const unsigned*>(row);
-                } else {
+                } else if constexpr (NSW >= 2) {
                     const u32x2 v = *reinterpret_cast<const u32x2*>(row);
                     sw[r][0] = v.x;
                     sw[r][1] = v.y;
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
                         sw[tt][r][0] = *reinterpret_cast<const unsigned short*>(row);
                     } else if constexpr (SROW == 4) {
                         sw[tt][r][0] = *reinterpret_cast<const unsigned*>(row);
-                    } else {
+                    } else if constexpr (NSW >= 2) {
                         const u32x2 v = *reinterpret_cast<const u32x2*>(row);
                         sw[tt][r][0] = v.x;
                         sw[tt][r][1] = v.y;

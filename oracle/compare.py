@@ -1,7 +1,11 @@
 """Element-by-element comparison of GPU outputs with the oracle (TEST INFRASTRUCTURE ONLY).
 
 Tolerances (fixed by the parity contract):
-  rotated fp32 values   max over rows of max|gpu - ref| / max|ref| <= 1e-5
+  rotated fp32 values   max over rows of max|gpu - ref| / max|ref| <= 1e-5 for Q rows
+                        (fp32 arithmetic: RoPE, pair rotation and log2 b butterfly
+                        roundings, amplified by at most sqrt(d) against the row
+                        max), 2^-23 for K and V rows (fp64 values exported to fp32:
+                        one rounding)
   Q output (bf16/fp32)  |out - ref| <= half an ulp of the output format at |ref|
                         + 1e-5 * max|ref row| (the fp32 allowance above)
   fp32 group scale s32  relative error <= 2^-23: both sides take the group absmax
@@ -21,6 +25,7 @@ import math
 import numpy as np
 
 ROW_REL_TOL = 1e-5
+KV_ROW_REL_TOL = 2.0 ** -23
 SCALE_REL_TOL = 2.0 ** -23
 CODE_BAND = 1e-9
 ANGLE_TOL = 1e-6
@@ -109,8 +114,8 @@ def compare_k(codes_gpu, scales_gpu_bits, k_rot_ref, scales_ref_bits, codes_ref,
     rep = {"rows": int(rows), "groups": int(rows * ng), "codes": int(rows * d)}
     if k_rot_gpu is not None:
         rep["k_row_rel_err"] = row_rel_err(k_rot_gpu, k_rot_ref)
-        if not rep["k_row_rel_err"] <= ROW_REL_TOL:
-            raise ParityError(f"rotated K row error {rep['k_row_rel_err']:.3g} > {ROW_REL_TOL}")
+        if not rep["k_row_rel_err"] <= KV_ROW_REL_TOL:
+            raise ParityError(f"rotated K row error {rep['k_row_rel_err']:.3g} > {KV_ROW_REL_TOL}")
     if s32_gpu is not None:
         g, r = s32_gpu.astype(np.float64).ravel(), s32_ref.astype(np.float64).ravel()
         bad = (r == 0) & (g != 0)

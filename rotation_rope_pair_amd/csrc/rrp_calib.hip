@@ -205,15 +205,27 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
 }
 
 // Per-key-head angle sets.  A block's kSetWaves waves take kSetWaves sets of one
-// stream (wave w: set sg * kSetWaves + w) and walk the same groups of
-// kSetWaves tokens: wave j builds the RoPE table of the group's token j into
-// LDS, so each token's table is built once per block instead of once per set,
-// and each wave then reads the rows (token j, head h) of its own set, flattened
-// over the group and cut into passes of RP rows.  A set with one head per
-// stream (the K stream) thus still fills every row group of a pass.  Each wave
-// writes its set's partials to column set * (nbq + nbk) + (block's place in the
-// set-group run), the layout calib_reduce_kernel reads.
+// stream (wave w: set sg * kSetWaves + w) and walk the same groups of TG tokens:
+// the waves build the RoPE tables of the group's tokens into LDS (token j by
+// wave j % kSetWaves), so each token's table is built once per block instead of
+// once per set, and each wave then reads the rows (token j, head h) of its own
+// set, flattened over the group and cut into passes of RP rows.  TG grows with
+// fewer heads per set, so that a wave has at least eight passes per group (and
+// per pair of barriers around the tables): at d = 128 the Q stream with four
+// heads per set takes 8 tokens, the K stream with one head per set 32.  Each wave writes its set's partials to column
+// set * (nbq + nbk) + (block's place in the set-group run), the layout
+// calib_reduce_kernel reads.
 constexpr int kSetWaves = 4;
+constexpr int kMaxSetGroup = 32;  // tokens per group, at most (32 KB of tables at d = 128)
+constexpr int kSetPasses = 8;     // row passes per wave and group, at least
+
+// Tokens per group of the per-set kernel for a stream with `heads` heads per set
+// and `rows_per_pass` rows in a pass (512 / head_dim).
+__host__ __device__ inline int set_group_tokens(int heads, int rows_per_pass) {
+    int tg = kSetWaves;
+    while (tg < kMaxSetGroup && tg * heads < kSetPasses * rows_per_pass) tg *= 2;
+    return tg;
+}
 
 template <typename E, int D, int LAYOUT, int MAXP>
 __global__ __launch_bounds__(64 * kSetWaves)
@@ -225,7 +237,7 @@ void calib_sets_kernel(const CalibArgs a) {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr size_t ROWB = (size_t)D * EB;
     using QT = typename Quad<E>::T;
-    __shared__ double2 tab[kSetWaves][P];
+    __shared__ double2 tab[kMaxSetGroup][P];
 
     const int lane = (int)__lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -247,7 +259,8 @@ void calib_sets_kernel(const CalibArgs a) {
     const int nh_all = is_k ? a.hk : a.hq;
     const int g = nh_all / a.n_sets;  // heads per set
     const int h0 = set * g;
-    const int nrows = kSetWaves * g;  // rows per token group
+    const int tg = set_group_tokens(g, RP);  // tokens per group (uniform per block)
+    const int nrows = tg * g;                // rows per token group
     const int npass = (nrows + RP - 1) / RP;
     const int nstep = (npass + MAXP - 1) / MAXP;
     const float invf = lane_inv_freq(a.inv_freq, lane, P);
@@ -260,11 +273,11 @@ void calib_sets_kernel(const CalibArgs a) {
 #pragma unroll
         for (int m = 0; m < kNSum; ++m) acc[j][m] = 0.0;
 
-    // Token groups bs, bs + nb, ...: tokens kSetWaves * group + j.
-    const int64_t n_groups = (a.n_tokens + kSetWaves - 1) / kSetWaves;
+    // Token groups bs, bs + nb, ...: tokens tg * group + j.
+    const int64_t n_groups = (a.n_tokens + tg - 1) / tg;
     auto row_valid = [&](int64_t grp_t, int r, int64_t& t, int& h) {
         const int j = r / g;
-        t = grp_t * kSetWaves + j;
+        t = grp_t * tg + j;
         h = h0 + (r - j * g);
         return active && r < nrows && t < a.n_tokens;
     };
@@ -303,11 +316,13 @@ void calib_sets_kernel(const CalibArgs a) {
         if (gn < n_groups) load_step(gn, sn_step, nxt);
         if (st == 0) {
             __syncthreads();  // the previous group's table reads are complete
-            const int64_t t = gt * kSetWaves + wave;
-            if (lane < P && t < a.n_tokens) {
-                double sa, ca;
-                sincos_f64_of_f32(rope_angle_f32(token_pos(a.pos, t), invf), sa, ca);
-                tab[wave][lane] = make_double2(ca, sa);
+            for (int jj = wave; jj < tg; jj += kSetWaves) {
+                const int64_t t = gt * tg + jj;
+                if (lane < P && t < a.n_tokens) {
+                    double sa, ca;
+                    sincos_f64_of_f32(rope_angle_f32(token_pos(a.pos, t), invf), sa, ca);
+                    tab[jj][lane] = make_double2(ca, sa);
+                }
             }
             __syncthreads();
         }
@@ -479,12 +494,17 @@ int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, in
         *nbq = 0;
         *nbk = total;
     } else {
-        // rows per token (one shared set) or per group of kSetWaves tokens (per-set kernel)
+        // Work per token: row passes plus tables.  One shared set: a wave's passes
+        // of one token and its table.  Per-set kernel: a wave's passes of a group
+        // of tg tokens and its tg / kSetWaves tables, over tg.
         const int rp = 512 / head_dim;  // rows per pass
-        const int tg = n_sets > 1 ? kSetWaves : 1;
-        const int64_t wq = (tg * (hq / n_sets) + rp - 1) / rp + RRP_CALIB_TABLE_WEIGHT;
-        const int64_t wk = (tg * (hk / n_sets) + rp - 1) / rp + RRP_CALIB_TABLE_WEIGHT;
-        int q = (int)((int64_t)total * wq / (wq + wk));
+        auto work = [&](int heads) {
+            if (n_sets == 1) return (double)((heads + rp - 1) / rp + RRP_CALIB_TABLE_WEIGHT);
+            const int g = heads / n_sets, tg = set_group_tokens(g, rp);
+            return ((double)((tg * g + rp - 1) / rp) + (double)RRP_CALIB_TABLE_WEIGHT * tg / kSetWaves) / tg;
+        };
+        const double wq = work(hq), wk = work(hk);
+        int q = (int)((double)total * wq / (wq + wk));
         if (q < 1) q = 1;
         if (q > total - 1) q = total - 1;
         *nbq = q;

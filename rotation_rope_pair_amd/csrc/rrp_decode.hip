@@ -205,18 +205,22 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
         };
 
         // A loads for the tile starting at key0: NM words (8 codes each) of key key0 + col.
+        // The code loads are plain (cached) loads: a slot's key-head rows share
+        // 128-byte lines (two heads at d = 128) that neighbouring waves of a block
+        // read, and with a nontemporal hint each half of a line came from HBM on
+        // its own (8-10 % slower on the decode batch).
         auto load_a = [&](int key0, unsigned (&w)[NM]) {
             const unsigned char* row = row_of(key0 + col, false);
             if constexpr (KBM && NM == 4) {
-                const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row));
+                const u32x4 v = *reinterpret_cast<const u32x4*>(row);
                 w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
             } else if constexpr (KBM) {
-                const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row));
+                const u32x2 v = *reinterpret_cast<const u32x2*>(row);
                 w[0] = v.x; w[1] = v.y;
             } else {
 #pragma unroll
                 for (int m = 0; m < NM; ++m)
-                    w[m] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(row + 16 * m));
+                    w[m] = *reinterpret_cast<const unsigned*>(row + 16 * m);
             }
         };
         // Scales of groups [g0, g0 + NS) of the lane's four D keys key0 + 4 kb + r, as fp32.
@@ -294,10 +298,10 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
 #pragma unroll
             for (int tt = 0; tt < TP; ++tt) {
                 if constexpr (NM == 4) {
-                    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cb + off_a[tt]));
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(cb + off_a[tt]);
                     w[tt][0] = v.x; w[tt][1] = v.y; w[tt][2] = v.z; w[tt][3] = v.w;
                 } else {
-                    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(cb + off_a[tt]));
+                    const u32x2 v = *reinterpret_cast<const u32x2*>(cb + off_a[tt]);
                     w[tt][0] = v.x; w[tt][1] = v.y;
                 }
 #pragma unroll

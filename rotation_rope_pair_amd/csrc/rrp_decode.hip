@@ -473,12 +473,13 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
                         o[r] = (slot >= 0 && slot < a.n_slots) ? acc[r] * descale : __builtin_nanf("");
                     }
                 }
+                // plain stores: the logits are read again by the softmax that follows
                 if (a.vec_store && kq + 3 < k_end) {
-                    __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out_row + kq));
+                    *reinterpret_cast<f32x4*>(out_row + kq) = o;
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (kq + r < k_end) __builtin_nontemporal_store(o[r], out_row + kq + r);
+                        if (kq + r < k_end) out_row[kq + r] = o[r];
                 }
             }
         };

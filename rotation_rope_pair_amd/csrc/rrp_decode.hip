@@ -40,7 +40,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #endif
 constexpr int kKeysPerWave = RRP_DECODE_KEYS_PER_WAVE;
 #ifndef RRP_DECODE_TILES_PER_STEP
-#define RRP_DECODE_TILES_PER_STEP 2
+#define RRP_DECODE_TILES_PER_STEP 1
 #endif
 constexpr int kTilesPerStep = RRP_DECODE_TILES_PER_STEP;  // 16-key tiles loaded per step
 

@@ -136,6 +136,13 @@ def decode_latency_us(dev, stream, reps=200):
     return out
 
 
+def settle(fn, ms_each, total_ms=25.0):
+    """Untimed launches worth about total_ms, so the clocks settle as before the
+    hot-path timing."""
+    for _ in range(max(3, int(total_ms / max(ms_each, 1e-3)))):
+        fn()
+
+
 def qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b, g, reps=50):
     """The same prefill launch with the V half of the KV4 cache written too
     (one more read stream: V rows through the full-head Hadamard into INT4)."""
@@ -148,8 +155,7 @@ def qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b
     def launch():
         rrp.rotate_quantize_qkv(shape, q, k, v, pos, support_b=b, group=g, k_codes=codes, k_scales=scales,
                                 v_codes=vc, v_scales=vs, angles=angles, q_out=q_out)
-    for _ in range(10):
-        launch()
+    settle(launch, 0.55)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
@@ -172,18 +178,20 @@ def per_head_timing(w, q, k, pos, q_out, codes, scales, dev, stream, b, g, reps=
     moments = rrp.new_moments(d, dev, n_sets=hk)
     angles = torch.empty((hk, d // 2), dtype=torch.float32, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
-    ev[0].record(stream)
-    for _ in range(10):
+
+    def calibrate():
         moments.zero_()
         rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
+    settle(calibrate, 0.4)
+    ev[0].record(stream)
+    for _ in range(20):
+        calibrate()
     ev[1].record(stream)
 
     def launch():
         rrp.rotate_quantize_qk(shape, q, k, pos, support_b=b, group=g, k_codes=codes, k_scales=scales,
                                angles=angles, q_out=q_out)
-    for _ in range(10):
-        launch()
+    settle(launch, 0.48)
     ev[2].record(stream)
     for _ in range(reps):
         launch()
@@ -191,11 +199,11 @@ def per_head_timing(w, q, k, pos, q_out, codes, scales, dev, stream, b, g, reps=
     torch.cuda.synchronize()
     ms = ev[2].elapsed_time(ev[3]) / reps
     nbytes = w.bytes_per_token(group=g, with_slot=False) * w.n_tokens
-    return {"per_head_calibrate_angles_ms": ev[0].elapsed_time(ev[1]) / 10,
+    return {"per_head_calibrate_angles_ms": ev[0].elapsed_time(ev[1]) / 20,
             "per_head_rotate_quantize_ms": ms, "per_head_rotate_hbm_gbs": nbytes / (ms * 1e-3) / 1e9}
 
 
-def decode_scores_timing(dev, stream, reps=20):
+def decode_scores_timing(dev, stream, reps=40):
     """rrp_decode_scores over the 256-sequence decode batch (Mistral-shaped, 32 / 8
     heads, d 128, g 64) reading its 256 x 32768-slot KV4 cache: time per launch and
     algorithmic GB/s (cache rows read + logits written + queries read)."""
@@ -216,8 +224,7 @@ def decode_scores_timing(dev, stream, reps=20):
     def launch():
         rrp.decode_scores(shape, q, codes, scales, group=bt["group"], seq_start=start, seq_len=lens,
                           max_len=bt["max_len"], scores=out)
-    for _ in range(3):
-        launch()
+    settle(launch, 0.6)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
@@ -272,11 +279,15 @@ def main():
     supporting = {}
     if not args.hot_path_only:
         reps = 10
+
+        def calibrate():
+            moments.zero_()
+            rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
+        settle(calibrate, 0.3)
         torch.cuda.synchronize()
         ev[0].record(stream)
         for _ in range(reps):
-            moments.zero_()
-            rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
+            calibrate()
         ev[1].record(stream)
         # Supporting pass 2: the K-range / quantisation-error diagnostic at b = 128.
         stats = torch.empty(8, dtype=torch.float64, device=dev)

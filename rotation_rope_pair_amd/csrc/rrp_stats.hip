@@ -29,24 +29,24 @@ struct StatAcc {
 template <int D, int CE, bool SMALLG>
 __device__ __forceinline__ void add_row_stats(const double (&y)[2][CE], int g, int s, StatAcc& acc) {
     constexpr int P = D / 2;
+    // The group's absmax is max(max, -min) (exact), so only max and min are reduced.
     if constexpr (!SMALLG) {
-        // one group value per chunk: absmax, max, min over the group
-        double ca[2], cx[2], cn[2];
+        // one group value per chunk: max, min over the group
+        double cx[2], cn[2], ca[2];
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-            ca[ch] = 0.0;
             cx[ch] = y[ch][0];
             cn[ch] = y[ch][0];
 #pragma unroll
-            for (int i2 = 0; i2 < CE; ++i2) {
-                ca[ch] = fmax(ca[ch], fabs(y[ch][i2]));
+            for (int i2 = 1; i2 < CE; ++i2) {
                 cx[ch] = fmax(cx[ch], y[ch][i2]);
                 cn[ch] = fmin(cn[ch], y[ch][i2]);
             }
         }
-        group_reduce_chunkwise<D, CE, true>(ca, g);
         group_reduce_chunkwise<D, CE, true>(cx, g);
         group_reduce_chunkwise<D, CE, false>(cn, g);
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) ca[ch] = fmax(cx[ch], -cn[ch]);
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
             const GroupScale64 gs = group_scale64(ca[ch]);
@@ -68,13 +68,15 @@ __device__ __forceinline__ void add_row_stats(const double (&y)[2][CE], int g, i
         for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
             for (int i2 = 0; i2 < CE; ++i2) {
-                am[ch][i2] = fabs(y[ch][i2]);
                 mx[ch][i2] = y[ch][i2];
                 mn[ch][i2] = y[ch][i2];
             }
-        group_reduce_inreg<CE, true>(am, g);
         group_reduce_inreg<CE, true>(mx, g);
         group_reduce_inreg<CE, false>(mn, g);
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int i2 = 0; i2 < CE; ++i2) am[ch][i2] = fmax(mx[ch][i2], -mn[ch][i2]);
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch)
 #pragma unroll

@@ -417,6 +417,24 @@ def test_calibration_parity(n, est):
     print(f"workload {n} {est}: moments {worst:.2e} {rep}")
 
 
+@pytest.mark.parametrize("T", [1, 5, 127, 129, 383])
+@pytest.mark.parametrize("est", ["default", "k_only"])
+@pytest.mark.parametrize("ah", [0, 8])
+def test_calibration_parity_small_batches(T, est, ah):
+    """Batches from one token to a few blocks' worth, with ragged tails: the
+    shared-set grid takes one block per 128 tokens, the per-set grid one per 32
+    tokens and stream over the sets (at least one per stream and set)."""
+    w = W.WORKLOADS[2]
+    inp = inputs(2)
+    q = inp["q"][:T] if est != "k_only" else None
+    k, pos = inp["k"][:T], inp["pos"][:T]
+    mom_g, ang_g = run_calib(w, q, k, pos, est, ah=ah)
+    mom_r = O.calibrate_moments(oshape_of(w, ah=ah), q, k, pos)
+    phi64, _, abc = O.angles_from_moments(mom_r, EST[est])
+    C.compare_moments(mom_g, mom_r)
+    C.compare_angles(ang_g.reshape(-1), phi64.reshape(-1), abc.reshape(-1, 3))
+
+
 def test_calibration_accumulates_and_finalises_separately():
     w, inp = W.WORKLOADS[2], inputs(2)
     q, k, pos = inp["q"], inp["k"], inp["pos"]

@@ -246,6 +246,15 @@ __device__ __forceinline__ void sincos_f64_of_f32(float alpha, double& s_out, do
 // wave's two LDS tables: fp64 (K rows) and the same values rounded once to
 // fp32 (Q rows).
 // ---------------------------------------------------------------------------
+// Shared-set tables hold one padding entry after every 8 pairs (entry of pair k
+// at k + k / 8).  The lanes of a row each read a block of consecutive pairs, so
+// without padding their entries sit 8 pairs apart and fall in the same LDS
+// banks; with it they fall in different ones (fp32 and fp64 entries alike).
+constexpr int kTabPad = 8;
+template <int P>
+constexpr int tab_entries() { return P + P / kTabPad; }
+__device__ __forceinline__ int tab_index(int k) { return k + k / kTabPad; }
+
 template <int D, bool FOLD>
 __device__ __forceinline__ void token_tables(float2* tab32, double2* tab64, int lane, int p, float invf,
                                              double cphi, double sphi, double rs) {
@@ -256,8 +265,9 @@ __device__ __forceinline__ void token_tables(float2* tab32, double2* tab64, int 
         sincos_f64_of_f32(rope_angle_f32(p, invf), sa, ca);
         const double C = (ca * cphi - sa * sphi) * rs, S = (sa * cphi + ca * sphi) * rs;
         const double e0 = FOLD ? C + S : C, e1 = FOLD ? C - S : S;
-        tab64[lane] = make_double2(e0, e1);
-        tab32[lane] = make_float2((float)e0, (float)e1);
+        const int e = tab_index(lane);
+        tab64[e] = make_double2(e0, e1);
+        tab32[e] = make_float2((float)e0, (float)e1);
     }
     wave_lds_sync();
 }

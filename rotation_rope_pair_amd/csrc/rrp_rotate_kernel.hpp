@@ -124,8 +124,8 @@ void rotate_quantize_kernel(const RotateArgs a) {
     constexpr int MQ = Depth<R>::Q, MK = Depth<R>::K;
     constexpr bool FOLD = (LAYOUT == 0) && (BT == D);
     constexpr int WMAX = PH ? kPerSetWaves : 4;  // waves per block
-    __shared__ float2 tab32_all[WMAX][PH ? (kPerSetQ64 ? 1 : kSetStride * P) : P];
-    __shared__ double2 tab64_all[WMAX][PH ? kSetStride * P : P];
+    __shared__ float2 tab32_all[WMAX][PH ? (kPerSetQ64 ? 1 : kSetStride * P) : tab_entries<P>()];
+    __shared__ double2 tab64_all[WMAX][PH ? kSetStride * P : tab_entries<P>()];
     __shared__ double2 phi_all[PH ? kSetStride * P : 1];
 
     const int lane = (int)__lane_id();
@@ -148,6 +148,9 @@ void rotate_quantize_kernel(const RotateArgs a) {
     if constexpr (PH) {
 #pragma unroll
         for (int j = 0; j < CE; ++j) kidx[j] *= kSetStride;  // pair-major per-set tables
+    } else {
+#pragma unroll
+        for (int j = 0; j < CE; ++j) kidx[j] = tab_index(kidx[j]);  // padded shared table
     }
 
     const int hq = a.hq_rows, hk = a.hk;

@@ -136,8 +136,8 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr size_t ROWB = (size_t)D * EB;
     constexpr bool FOLD = (LAYOUT == 0) && (BT == D);
-    __shared__ float2 tab32_all[4][PH ? 1 : P];  // fp32 tables (unused by per-set tables)
-    __shared__ double2 tab64_all[4][PH ? kSetStride * P : P];
+    __shared__ float2 tab32_all[4][PH ? 1 : tab_entries<P>()];  // fp32 tables (unused by per-set tables)
+    __shared__ double2 tab64_all[4][PH ? kSetStride * P : tab_entries<P>()];
     __shared__ double2 phi_all[PH ? kSetStride * P : 1];
     __shared__ double red[4][kNStat];
 
@@ -159,6 +159,9 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
     if constexpr (PH) {
 #pragma unroll
         for (int j = 0; j < CE; ++j) kidx[j] *= kSetStride;  // pair-major per-set tables
+    } else {
+#pragma unroll
+        for (int j = 0; j < CE; ++j) kidx[j] = tab_index(kidx[j]);  // padded shared table
     }
     const unsigned char* kb = static_cast<const unsigned char*>(a.k);
     const int npass = (a.hk + R - 1) / R;
@@ -296,8 +299,8 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr size_t ROWB = (size_t)D * EB;
     constexpr int NJ = J1 - J0;
-    __shared__ float2 tab32_all[4][PH ? 1 : P];  // fp32 tables (unused by per-set tables)
-    __shared__ double2 tab64_all[4][PH ? kSetStride * P : P];
+    __shared__ float2 tab32_all[4][PH ? 1 : tab_entries<P>()];  // fp32 tables (unused by per-set tables)
+    __shared__ double2 tab64_all[4][PH ? kSetStride * P : tab_entries<P>()];
     __shared__ double2 phi_all[PH ? kSetStride * P : 1];
     __shared__ double red[4][kNStat];
 
@@ -318,6 +321,9 @@ __global__ __launch_bounds__(256) void stats_sweep_kernel(const StatsArgs a) {
     if constexpr (PH) {
 #pragma unroll
         for (int j = 0; j < CE; ++j) kidx[j] *= kSetStride;  // pair-major per-set tables
+    } else {
+#pragma unroll
+        for (int j = 0; j < CE; ++j) kidx[j] = tab_index(kidx[j]);  // padded shared table
     }
     const unsigned char* kb = static_cast<const unsigned char*>(a.k);
     const int npass = (a.hk + R - 1) / R;

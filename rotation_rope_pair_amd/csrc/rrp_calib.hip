@@ -481,11 +481,11 @@ hipError_t launch_t(const CalibArgs& a, hipStream_t st) {
 #endif
 
 int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, int n_sets, int* nbq, int* nbk) {
-    // One shared set: one block per 128 tokens, Q and K streams together (a wave
-    // walks about 64 tokens of Q or K with K only, 32 with Q: fewer, longer waves
-    // than that spend less on starting up and on writing partials; measured
-    // best against 32 to 512 tokens per block).  Per-set calibration: about 8
-    // tokens per wave per stream.  At most kMaxCalibBlocks partial columns over
+    // One shared set: one block per 128 tokens for both streams together, so a
+    // wave walks 32 tokens with K only and more with Q (the streams share the
+    // blocks by work); measured best against 32 to 512 tokens per block, since
+    // shorter waves spend more on starting up and on writing partials.  Per-set
+    // calibration: about 8 tokens per wave per stream.  At most kMaxCalibBlocks partial columns over
     // all sets.  The streams share a set's blocks in proportion to their work
     // per token (per token group for per-set calibration): the row passes plus
     // the table (worth about RRP_CALIB_TABLE_WEIGHT passes).

@@ -144,13 +144,22 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
 
     const int lane = (int)__lane_id();
     // wave-uniform (scalar) indices, so row bases stay in scalar registers
-    const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) +
-                        __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int hk = a.hk;
-    const int kvh = (int)(wid % hk);
-    const int64_t rest = wid / hk;
-    const int chunk = (int)(rest % a.n_chunks);
-    const int64_t b = rest / a.n_chunks;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    int kvh, chunk;
+    int64_t b;
+    if (a.grid3d) {
+        // grid (hk / 4, chunks, sequences): the indices need no division
+        kvh = (int)blockIdx.x * 4 + wave;
+        chunk = (int)blockIdx.y;
+        b = blockIdx.z;
+    } else {
+        const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+        kvh = (int)(wid % hk);
+        const int64_t rest = wid / hk;
+        chunk = (int)(rest % a.n_chunks);
+        b = rest / a.n_chunks;
+    }
     if (b >= a.n_seqs) return;
     int len = a.seq_len[b];
     len = len < a.max_len ? len : a.max_len;
@@ -518,10 +527,20 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
 }
 
 template <typename E, int D>
-hipError_t launch_d(const DecodeArgs& a, int group, hipStream_t st) {
-    const int64_t waves = a.n_seqs * a.n_chunks * a.hk;
-    const int64_t blocks = (waves + 3) / 4;
-    const dim3 grid((unsigned)blocks), block(256);
+hipError_t launch_d(const DecodeArgs& a0, int group, hipStream_t st) {
+    // Four key heads of one (sequence, chunk) per block.  With hk a multiple of 4
+    // (and the chunk and sequence counts within the y and z grid limits) the
+    // block's place comes straight from a 3-D grid, else from a 1-D one.
+    DecodeArgs a = a0;
+    dim3 grid;
+    a.grid3d = (a.hk % 4 == 0 && a.n_chunks <= 65535 && a.n_seqs <= 65535) ? 1 : 0;
+    if (a.grid3d) {
+        grid = dim3((unsigned)(a.hk / 4), (unsigned)a.n_chunks, (unsigned)a.n_seqs);
+    } else {
+        const int64_t waves = a.n_seqs * a.n_chunks * a.hk;
+        grid = dim3((unsigned)((waves + 3) / 4));
+    }
+    const dim3 block(256);
 #define RRP_G(GS) \
     if (group == GS) { hipLaunchKernelGGL((decode_scores_kernel<E, D, GS>), grid, block, 0, st, a); return hipGetLastError(); }
     RRP_G(2) RRP_G(4) RRP_G(8) RRP_G(16) RRP_G(32) RRP_G(64)

@@ -77,6 +77,7 @@ struct DecodeArgs {
     int32_t group_heads;       // hq / hk query heads per key head
     int32_t max_len;
     int32_t vec_store;         // scores rows are 16-byte aligned: store 4 logits at once
+    int32_t grid3d;            // grid (hk / 4, n_chunks, n_seqs) instead of one dimension (set by the launcher)
 };
 
 

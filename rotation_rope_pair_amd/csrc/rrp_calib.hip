@@ -456,29 +456,29 @@ __global__ __launch_bounds__(512) void calib_angles_kernel(const CalibFinalArgs 
     a.angles_out[k] = (float)phi;
 }
 
-#ifndef RRP_CALIB_MAXP
-#define RRP_CALIB_MAXP 2
-#endif
+// Row passes of a stream kept in flight per wave (the next step's rows are
+// loaded while the current step is accumulated).
+constexpr int kCalibMaxPasses = 2;
 
 template <typename E, int D, int LAYOUT>
 hipError_t launch_t(const CalibArgs& a, hipStream_t st) {
     if (a.n_sets > 1) {
         const int groups = (a.n_sets + kSetWaves - 1) / kSetWaves;
         const int blocks = (a.nbq + a.nbk) * groups;
-        hipLaunchKernelGGL((calib_sets_kernel<E, D, LAYOUT, RRP_CALIB_MAXP>), dim3(blocks), dim3(64 * kSetWaves), 0,
+        hipLaunchKernelGGL((calib_sets_kernel<E, D, LAYOUT, kCalibMaxPasses>), dim3(blocks), dim3(64 * kSetWaves), 0,
                            st, a);
         return hipGetLastError();
     }
     const int blocks = a.nbq + a.nbk;
-    hipLaunchKernelGGL((calib_moments_kernel<E, D, LAYOUT, RRP_CALIB_MAXP>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((calib_moments_kernel<E, D, LAYOUT, kCalibMaxPasses>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-#ifndef RRP_CALIB_TABLE_WEIGHT
-#define RRP_CALIB_TABLE_WEIGHT 2
-#endif
+// Cost of one token's RoPE table build, counted in row passes, when a set's
+// blocks are split between the Q and K streams by work rather than by rows.
+constexpr int kCalibTableWeight = 2;
 
 int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, int n_sets, int* nbq, int* nbk) {
     // One shared set: one block per 128 tokens for both streams together, so a
@@ -488,7 +488,7 @@ int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, in
     // calibration: about 8 tokens per wave per stream.  At most kMaxCalibBlocks partial columns over
     // all sets.  The streams share a set's blocks in proportion to their work
     // per token (per token group for per-set calibration): the row passes plus
-    // the table (worth about RRP_CALIB_TABLE_WEIGHT passes).
+    // the table (worth about kCalibTableWeight passes).
     int64_t want = n_sets == 1 ? (n_tokens + 127) / 128 : (n_tokens * (with_q ? 2 : 1) + 31) / 32;
     if (want > kMaxCalibBlocks) want = kMaxCalibBlocks;
     want /= n_sets;  // per set (so all sets together stay within kMaxCalibBlocks)
@@ -503,9 +503,9 @@ int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, in
         // of tg tokens and its tg / kSetWaves tables, over tg.
         const int rp = 512 / head_dim;  // rows per pass
         auto work = [&](int heads) {
-            if (n_sets == 1) return (double)((heads + rp - 1) / rp + RRP_CALIB_TABLE_WEIGHT);
+            if (n_sets == 1) return (double)((heads + rp - 1) / rp + kCalibTableWeight);
             const int g = heads / n_sets, tg = set_group_tokens(g, rp);
-            return ((double)((tg * g + rp - 1) / rp) + (double)RRP_CALIB_TABLE_WEIGHT * tg / kSetWaves) / tg;
+            return ((double)((tg * g + rp - 1) / rp) + (double)kCalibTableWeight * tg / kSetWaves) / tg;
         };
         const double wq = work(hq), wk = work(hk);
         int q = (int)((double)total * wq / (wq + wk));

@@ -11,14 +11,10 @@ namespace rrp {
 
 namespace {
 
-#ifndef RRP_K_FP64
-#define RRP_K_FP64 1
-#endif
-#if RRP_K_FP64
+// K and V rows are transformed and quantised in fp64: the group scales and
+// codes are integer decisions taken from y, made in the precision of their
+// definition for every group size.
 typedef double KV;
-#else
-typedef float KV;
-#endif
 
 // Quantise one K row held as y[2][CE] (output order) in lane s; write codes / scales.
 // SMALLG: groups smaller than one 16-byte chunk (g < CE), reduced in registers.
@@ -85,13 +81,11 @@ __device__ __forceinline__ void load_row_chunks(const unsigned char* __restrict_
         r[ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + chunk_offset<E, D>(ch, s_src)));
 }
 
-// Passes kept in flight per token: Q rows and K rows of one token for the
-// Llama / Mistral head counts (32 Q + 8 KV heads at 8 rows per pass).
-#ifndef RRP_DEPTH_Q
-#define RRP_DEPTH_Q 1
-#endif
+// Row passes kept in flight per token: one Q pass (two Q passes measured
+// slower: 155 instead of 136 VGPRs, two instead of three waves per SIMD) and
+// one K pass (two when a pass holds fewer than 8 rows).
 template <int R> struct Depth {
-    static constexpr int Q = R >= 16 ? (RRP_DEPTH_Q + 1) / 2 : RRP_DEPTH_Q;
+    static constexpr int Q = 1;
     static constexpr int K = R >= 8 ? 1 : 2;
 };
 
@@ -104,14 +98,7 @@ template <int R> struct Depth {
 // of the shared path's fp32 table); with the block's cos / sin of the sets
 // (9 KB), blocks of kPerSetWaves = 4 waves take 46 KB, three per CU.
 // SPLIT: each token's row passes are shared by a.split waves (small batches).
-#ifndef RRP_PH_WAVES
-#define RRP_PH_WAVES 4
-#endif
-#ifndef RRP_PH_Q64
-#define RRP_PH_Q64 1
-#endif
-constexpr int kPerSetWaves = RRP_PH_WAVES;
-constexpr bool kPerSetQ64 = RRP_PH_Q64;  // Q reads the fp64 per-set tables
+constexpr int kPerSetWaves = 4;
 
 template <typename E, int D, int LAYOUT, bool SMALLG, int BT, bool HAS_V, bool PH, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, PH ? 64 * kPerSetWaves : 256)))
@@ -124,7 +111,7 @@ void rotate_quantize_kernel(const RotateArgs a) {
     constexpr int MQ = Depth<R>::Q, MK = Depth<R>::K;
     constexpr bool FOLD = (LAYOUT == 0) && (BT == D);
     constexpr int WMAX = PH ? kPerSetWaves : 4;  // waves per block
-    __shared__ float2 tab32_all[WMAX][PH ? (kPerSetQ64 ? 1 : kSetStride * P) : tab_entries<P>()];
+    __shared__ float2 tab32_all[WMAX][PH ? 1 : tab_entries<P>()];
     __shared__ double2 tab64_all[WMAX][PH ? kSetStride * P : tab_entries<P>()];
     __shared__ double2 phi_all[PH ? kSetStride * P : 1];
 
@@ -209,8 +196,7 @@ void rotate_quantize_kernel(const RotateArgs a) {
         }
 
         if constexpr (PH)
-            token_tables_sets<D, FOLD>(kPerSetQ64 ? nullptr : tab32, tab64, lane, p, invf, phi_all, a.angle_sets,
-                                       a.rsqrt_b);
+            token_tables_sets<D, FOLD>(nullptr, tab64, lane, p, invf, phi_all, a.angle_sets, a.rsqrt_b);
         else token_tables<D, FOLD>(tab32, tab64, lane, p, invf, cphi, sphi, a.rsqrt_b);
 
         // ---- Q rows (fp32) ----
@@ -233,8 +219,7 @@ void rotate_quantize_kernel(const RotateArgs a) {
                 if constexpr (PH) {
                     // set of query head h: floor((h + 1/2) * sets / Hq), exact in fp32
                     const int qset = (int)(((float)h + 0.5f) * a.q_set_scale);
-                    if constexpr (kPerSetQ64) rotate_lds<LAYOUT, FOLD>(x, tab64 + qset, kidx);
-                    else rotate_lds<LAYOUT, FOLD>(x, tab32 + qset, kidx);
+                    rotate_lds<LAYOUT, FOLD>(x, tab64 + qset, kidx);
                 } else {
                     rotate_lds<LAYOUT, FOLD>(x, tab32, kidx);
                 }
@@ -279,8 +264,7 @@ void rotate_quantize_kernel(const RotateArgs a) {
 #pragma unroll
                     for (int i2 = 0; i2 < CE; ++i2) x[ch][i2] = (KV)xf[ch][i2];
                 const int kset = PH ? h : 0;  // key head h uses set h
-                if constexpr (RRP_K_FP64) rotate_lds<LAYOUT, FOLD>(x, tab64 + kset, kidx);
-                else rotate_lds<LAYOUT, FOLD>(x, tab32 + kset, kidx);
+                rotate_lds<LAYOUT, FOLD>(x, tab64 + kset, kidx);
                 fwht_row<D, CE, BT, FOLD>(x, a.support_b, s);
                 const size_t trow = (size_t)t * hk + h;
                 if (a.k_dbg) {
@@ -348,6 +332,9 @@ void rotate_quantize_kernel(const RotateArgs a) {
 // split over up to kSmallBatchWaves / T waves, at most one pass each, so a
 // decode batch is not serialised on one wave per token).
 constexpr int kSmallBatchWaves = 4096;
+// Grid cap of the large-batch family: waves then walk several tokens each
+// (caps of 2K, 4K, 16K and 32K blocks measured slower at the 128K prefill).
+constexpr int64_t kMaxRotateBlocks = 8192;
 
 template <typename E, int D, int LAYOUT, bool SPLIT>
 hipError_t launch_t(const RotateArgs& args, hipStream_t st) {
@@ -365,10 +352,7 @@ hipError_t launch_t(const RotateArgs& args, hipStream_t st) {
         a.split = split < 1 ? 1 : (int)split;
     }
     int64_t blocks = (a.n_tokens * a.split + wpb - 1) / wpb;
-#ifndef RRP_MAX_BLOCKS
-#define RRP_MAX_BLOCKS 8192
-#endif
-    if (blocks > RRP_MAX_BLOCKS) blocks = RRP_MAX_BLOCKS;  // waves then walk several tokens each
+    if (blocks > kMaxRotateBlocks) blocks = kMaxRotateBlocks;
     const bool smallg = a.group < Geo<E, D>::CE;
     const dim3 grid((unsigned)blocks), block(64 * wpb);
 #define RRP_LAUNCH(SG, BT, HV, PHV) \

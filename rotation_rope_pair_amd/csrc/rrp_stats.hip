@@ -412,10 +412,7 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const StatsFinalArgs a
 
 // The sweep's supports are split over kSweepParts launches (each keeps its
 // supports' sums in registers and reads K once).
-#ifndef RRP_SWEEP_PARTS
-#define RRP_SWEEP_PARTS 4
-#endif
-constexpr int kSweepParts = RRP_SWEEP_PARTS;
+constexpr int kSweepParts = 4;
 
 template <typename E, int D, int LAYOUT, bool SG, bool PH, int J0, int NB, int W>
 void launch_sweep_parts(const StatsArgs& a, int n_blocks, hipStream_t st) {

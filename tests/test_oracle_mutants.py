@@ -61,7 +61,7 @@ def _run_mutant(name, tmpdir):
 
 
 def test_every_planted_mistake_fails_a_pin(tmp_path):
-    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(2, min(8, os.cpu_count() or 2))) as ex:
         results = list(ex.map(lambda n: _run_mutant(n, str(tmp_path)), MUTANTS))
     survivors = [n for n, rc in results if rc == 0]
     assert not survivors, f"mutants not caught by any pin: {survivors}"

@@ -753,3 +753,100 @@ def test_stats_and_sweep_parity_interleaved_pairs(n, g, ah):
             rel = np.abs(got[:5] - r[:5]) / np.maximum(np.abs(r[:5]), 1e-300)
             assert np.all(rel <= STAT_TOL), (b, got, r, rel)
             assert got[5] == r[5] and got[6] == r[6]
+
+
+# ---------------------------------------------------------------------------
+# The large-batch kernel family (4096 tokens or more: one wave per token, waves
+# walking the batch with a grid stride of 8192 blocks x 4 waves = 32768 tokens)
+# against the oracle, for every compile-time variant a prefill can reach:
+# runtime support b < d, groups smaller than a 16-byte chunk, interleaved pairs,
+# fp32 rows, head_dim 64, per-key-head angle sets and the V half.  Batches are
+# longer than one grid-stride round, and the sampled tokens include both ends of
+# every round, the last one in particular.
+# ---------------------------------------------------------------------------
+
+GRID_STRIDE_TOKENS = 8192 * 4  # tokens per grid-stride round of the large-batch family
+
+
+def grid_sample(T, n, seed):
+    """n sampled tokens of a T-token batch plus the first and last token of every
+    grid-stride round."""
+    assert T >= 4096
+    edges = []
+    for r0 in range(0, T, GRID_STRIDE_TOKENS):
+        edges += [r0, min(T, r0 + GRID_STRIDE_TOKENS) - 1]
+    return np.unique(np.concatenate([sample_tokens(T, n, seed), np.array(edges)]))
+
+
+def long_inputs(n, T):
+    key = ("long", n, T)
+    if key not in _INPUTS:
+        _INPUTS[key] = W.make_inputs(n, n_tokens=T)
+    return _INPUTS[key]
+
+
+@pytest.mark.parametrize("ah", [0, 8])
+@pytest.mark.parametrize("b", [1, 2, 16, 64])
+def test_grid_stride_prefill_128k_support_sweep(b, ah):
+    """The 131072-token prefill (four grid-stride rounds) at b < d, shared and
+    per-key-head angles, in the benchmark's launch configuration."""
+    w, inp = W.WORKLOADS[4], inputs(4)
+    ang = random_angle_sets(w, 2000 + b) if ah else random_angles(w.n_pairs, 2000 + b)
+    out = run_rotate(w, inp, ang, b, 128, debug=False, ah=ah)
+    idx = grid_sample(w.n_tokens, 768, 2000 + b + ah)
+    assert idx.max() == w.n_tokens - 1 and (idx >= 3 * GRID_STRIDE_TOKENS).sum() > 100
+    print(b, ah, check_rotate(w, inp, out, ang, b, 128, idx, ah=ah))
+
+
+@pytest.mark.parametrize("b", [2, 128])
+@pytest.mark.parametrize("g", [2, 4, 16])
+def test_grid_stride_prefill_128k_small_groups(g, b):
+    """Groups of 2 and 4 channels (reduced inside a lane) and 16 (across two lanes)
+    on the full prefill."""
+    w, inp = W.WORKLOADS[4], inputs(4)
+    ang = random_angles(w.n_pairs, 2100 + g)
+    out = run_rotate(w, inp, ang, b, g, debug=False)
+    print(g, b, check_rotate(w, inp, out, ang, b, g, grid_sample(w.n_tokens, 512, 2100 + g + b)))
+
+
+@pytest.mark.parametrize("b,ah", [(128, 0), (16, 0), (2, 8)])
+def test_grid_stride_prefill_128k_interleaved_pairs(b, ah):
+    w, inp = W.WORKLOADS[4], inputs(4)
+    ang = random_angle_sets(w, 2200 + b) if ah else random_angles(w.n_pairs, 2200 + b)
+    out = run_rotate(w, inp, ang, b, 128, debug=False, layout=1, ah=ah)
+    print(b, ah, check_rotate(w, inp, out, ang, b, 128, grid_sample(w.n_tokens, 512, 2200 + b), layout=1, ah=ah))
+
+
+@pytest.mark.parametrize("b,g,layout", [(2, 64, 0), (64, 64, 0), (8, 2, 0), (32, 16, 1), (1, 64, 1)])
+def test_grid_stride_fp32_rows_tiny_shape(b, g, layout):
+    """fp32 rows of the tiny workload's shape (2 Q / 1 KV heads, d 64) over 40960
+    tokens (two grid-stride rounds), with the fp32 debug copies."""
+    w = W.WORKLOADS[1]
+    T = 40960
+    inp = long_inputs(1, T)
+    ang = random_angles(w.n_pairs, 2300 + b)
+    out = run_rotate(w, inp, ang, b, g, layout=layout)
+    print(b, g, layout, check_rotate(w, inp, out, ang, b, g, grid_sample(T, 2048, 2300 + b), layout=layout))
+
+
+@pytest.mark.parametrize("b,g,ah", [(2, 64, 0), (16, 64, 0), (32, 4, 0), (64, 64, 8), (4, 16, 8)])
+def test_grid_stride_head_dim_64(b, g, ah):
+    """head_dim 64 (the 1B layer's 32 / 8 heads) over 40960 tokens, with the fp32
+    debug copies."""
+    w = W.WORKLOADS[2]
+    T = 40960
+    inp = long_inputs(2, T)
+    ang = random_angle_sets(w, 2400 + b) if ah else random_angles(w.n_pairs, 2400 + b)
+    out = run_rotate(w, inp, ang, b, g, ah=ah)
+    print(b, g, ah, check_rotate(w, inp, out, ang, b, g, grid_sample(T, 768, 2400 + b), ah=ah))
+
+
+@pytest.mark.parametrize("b,g,ah", [(2, 4, 0), (16, 128, 8)])
+def test_grid_stride_prefill_128k_with_v(b, g, ah):
+    """The V half at b < d and a small group on the full prefill."""
+    w = W.WORKLOADS[4]
+    inp = vinputs(4)
+    ang = random_angle_sets(w, 2500 + b) if ah else random_angles(w.n_pairs, 2500 + b)
+    out = run_rotate_qkv(w, inp, ang, b, g, debug=False, ah=ah)
+    idx = grid_sample(w.n_tokens, 512, 2500 + b)
+    print(b, g, ah, check_rotate(w, inp, out, ang, b, g, idx, ah=ah), check_v(w, inp, out, g, idx))

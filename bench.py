@@ -9,8 +9,11 @@ timed region.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 50] [--no-cpu-baseline] [--hot-path-only]
 
-A step takes about half a millisecond, so the defaults time about 0.1 s of
-launches after about 25 ms of warm-up launches (clocks settle).
+A step takes about half a millisecond.  After the --warmup launches, at
+least 100 ms of untimed launches run back to back (the clocks settle; the
+first few tens of launches of a process are slower) before the timed window,
+whatever --warmup says; the JSON line records that settle time and its launch
+count, and the per-launch median, min and max beside the mean.
 
 --hot-path-only skips the supporting passes, the decode timing and the CPU
 baseline (short runs under a profiler).  Every run also times a plain
@@ -136,11 +139,34 @@ def decode_latency_us(dev, stream, reps=200):
     return out
 
 
+SETTLE_MS = 100.0  # untimed back-to-back launches before the hot-path window
+
+
 def settle(fn, ms_each, total_ms=25.0):
-    """Untimed launches worth about total_ms, so the clocks settle as before the
-    hot-path timing."""
+    """Untimed launches worth about total_ms, so the clocks settle before a
+    supporting timing."""
     for _ in range(max(3, int(total_ms / max(ms_each, 1e-3)))):
         fn()
+
+
+def settle_for(fn, stream, total_ms):
+    """Untimed launches of fn until at least total_ms of GPU time has passed
+    (measured with events on `stream`); returns the number of launches."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n, batch = 0, 8
+    e0.record(stream)
+    while True:
+        for _ in range(batch):
+            fn()
+        n += batch
+        e1.record(stream)
+        e1.synchronize()
+        spent = e0.elapsed_time(e1)
+        if spent >= total_ms:
+            return n
+        # enqueue the rest in one go (no host wait between launches)
+        batch = max(8, int((total_ms - spent) / max(spent / n, 1e-3)) + 1)
 
 
 def qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b, g, reps=50):
@@ -329,15 +355,21 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    # Whatever --warmup says, the timed window starts only after at least
+    # SETTLE_MS of back-to-back launches: the first tens of launches of a fresh
+    # process run slower while the clocks settle.
+    settle_launches = settle_for(step, stream, SETTLE_MS)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ev[4].record(stream)
-    for _ in range(args.steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev[5].record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms = ev[4].elapsed_time(ev[5]) / args.steps
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_launch = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
     bytes_per_launch = w.bytes_per_token(group=g, with_slot=False) * T
     achieved = bytes_per_launch / (ms * 1e-3) / 1e9
@@ -368,6 +400,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(per_launch)),
+        "ms_per_step_min": float(per_launch.min()),
+        "ms_per_step_max": float(per_launch.max()),
+        "settle_ms": SETTLE_MS,
+        "settle_launches": settle_launches,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

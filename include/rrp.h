@@ -20,8 +20,15 @@
  *     enqueued; the caller synchronises before reading outputs.
  *   - Arguments are validated on the host before anything is enqueued.  On an
  *     error the function returns a non-zero rrp_status and enqueues nothing.
- *     RRP_ERR_HIP reports a failed HIP runtime call (launch or stream-ordered
- *     allocation); work enqueued before the failing call may have run.
+ *     RRP_ERR_HIP reports a failed kernel launch; work enqueued before the
+ *     failing launch may have run.
+ *   - The library allocates no memory.  Calibration and diagnostics keep their
+ *     per-block partial sums in a caller-owned device workspace whose size the
+ *     matching *_workspace_size query gives for the same shape and token count;
+ *     a NULL or smaller workspace is RRP_ERR_INVALID_ARG, one not 8-byte aligned
+ *     RRP_ERR_MISALIGNED (both before anything is enqueued).  The workspace is
+ *     used by the enqueued work only: it may be reused by work enqueued later
+ *     on the same stream, and two calls in flight at once need two workspaces.
  *   - Tensors are dense, row-major, token-major: Q is [n_tokens][n_q_heads]
  *     [head_dim], K is [n_tokens][n_kv_heads][head_dim], in `dtype`.
  *   - Q, K and Q-output pointers must be 16-byte aligned (128-bit accesses).
@@ -31,6 +38,7 @@
 #ifndef RRP_H
 #define RRP_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -158,6 +166,13 @@ int rrp_rotate_quantize_qkv(const rrp_shape* shape, int32_t dtype, const void* q
                             float* k_rot_f32, float* k_scale_f32, float* v_rot_f32, float* v_scale_f32,
                             void* stream);
 
+/* Workspace bytes (written to *bytes, host) of one rrp_calibrate_angles call
+ * with this shape and token count; with_q != 0 when q is not NULL.  0 when
+ * n_tokens == 0.  At most 4096 * head_dim/2 * 5 * 8 bytes (10.5 MB at head_dim
+ * 128).  Errors: an invalid shape (as the entry point), n_tokens < 0 or
+ * bytes == NULL. */
+int rrp_calibrate_angles_workspace_size(const rrp_shape* shape, int64_t n_tokens, int32_t with_q, size_t* bytes);
+
 /* rrp_calibrate_angles -- the calibration pass ("optimisation objective" and
  * "estimator strategies" sections: a closed-form shared angle per pair that
  * minimises the larger of the pair's two channel variances under a
@@ -178,11 +193,12 @@ int rrp_rotate_quantize_qkv(const rrp_shape* shape, int32_t dtype, const void* q
  *
  * q may be NULL (Q stream not accumulated); then estimator must be K_ONLY.
  * n_tokens == 0 only finalises (if angles_out != NULL).
- * Allocates a scratch buffer of at most 4096 * head_dim/2 * 5 doubles
- * stream-ordered (hipMallocAsync / hipFreeAsync) on `stream`. */
+ * workspace     device, workspace_bytes >= rrp_calibrate_angles_workspace_size
+ *               (shape, n_tokens, q != NULL); may be NULL when that size is 0. */
 int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
                          const int32_t* pos, int64_t n_tokens, int32_t estimator,
-                         double* moments, float* angles_out, void* stream);
+                         double* moments, float* angles_out, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* rrp_quant_error_stats -- the diagnostic pass ("contributions" and "results"
  * sections: K range and relative quantisation error along the block-Hadamard
@@ -193,28 +209,39 @@ int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const void* q, c
  *                            sum of group max|y|, max of group max|y|,
  *                            sum of group (max y - min y), n_groups, n_rows, 0 }
  * (overwritten).  Relative error = sqrt(E / N); mean K range = [2] / [5].
- * Reduced in a fixed order (bit-reproducible).  Allocates a stream-ordered
- * scratch buffer of at most 4096 * 5 doubles on `stream`. */
+ * Reduced in a fixed order (bit-reproducible).
+ * workspace     device, workspace_bytes >= rrp_quant_error_stats_workspace_size
+ *               (shape, n_tokens); may be NULL when that size is 0. */
 int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
                           int64_t n_tokens, const float* angles, int32_t support_b, int32_t group,
-                          double* stats_out, void* stream);
+                          double* stats_out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* rrp_quant_error_sweep -- the support interpolation in one pass ("contributions"
+/* Workspace bytes (host *bytes) of one rrp_quant_error_stats call: at most
+ * 4096 * 5 * 8.  Errors as rrp_calibrate_angles_workspace_size. */
+int rrp_quant_error_stats_workspace_size(const rrp_shape* shape, int64_t n_tokens, size_t* bytes);
+
+/* rrp_quant_error_sweep -- the support interpolation in one call ("contributions"
  * and "results" sections: K range and relative quantisation error as the block
- * Hadamard support grows from 2 to head_dim).  Reads K twice (one launch per
- * half of the supports) and writes, for
- * every support b = 2^j, j = 0 .. log2(head_dim) (b = 1: no Hadamard), the
- * statistics rrp_quant_error_stats gives at that b (same angles and group):
+ * Hadamard support grows from 2 to head_dim).  Writes, for every support
+ * b = 2^j, j = 0 .. log2(head_dim) (b = 1: no Hadamard), the statistics
+ * rrp_quant_error_stats gives at that b (same angles and group):
  *   stats_out  double[log2(head_dim) + 1][8], row j = { E, N, sum of group max|y|,
  *              max of group max|y|, sum of group (max y - min y), n_groups,
  *              n_rows, b }  (overwritten).
  * Each row matches a separate rrp_quant_error_stats call up to the order of
  * fp64 rounding (the transform of support 2^j is built from the one of support
- * 2^(j-1) by one more butterfly stage).  Allocates a stream-ordered scratch
- * buffer of at most 4096 * 8 * 5 doubles on `stream`.  Errors as
- * rrp_quant_error_stats. */
+ * 2^(j-1) by one more butterfly stage).
+ * workspace     device, workspace_bytes >= rrp_quant_error_sweep_workspace_size
+ *               (shape, n_tokens); may be NULL when that size is 0.
+ * Errors as rrp_quant_error_stats. */
 int rrp_quant_error_sweep(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
-                          int64_t n_tokens, const float* angles, int32_t group, double* stats_out, void* stream);
+                          int64_t n_tokens, const float* angles, int32_t group, double* stats_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes (host *bytes) of one rrp_quant_error_sweep call: at most
+ * 4096 * (log2(head_dim) + 1) * 5 * 8.  Errors as
+ * rrp_calibrate_angles_workspace_size. */
+int rrp_quant_error_sweep_workspace_size(const rrp_shape* shape, int64_t n_tokens, size_t* bytes);
 
 /* rrp_decode_scores -- decode attention logits read straight from the KV4 cache
  * (LLM rotation-quantisation notes, section 3.2.1: the head-wise rotation

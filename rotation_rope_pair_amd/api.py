@@ -60,6 +60,41 @@ def _stream_ptr(stream, device) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _workspace(func, nbytes, workspace, stream, device):
+    """(pointer, size) of the device workspace of one call: the caller's
+    `workspace` tensor if given (checked for size), else a fresh uint8 tensor
+    from torch's caching allocator, tied to the stream the call runs on."""
+    if workspace is not None:
+        _dev(workspace, "workspace", device=device)
+        have = workspace.numel() * workspace.element_size()
+        if have < nbytes:
+            raise ValueError(f"{func}: workspace holds {have} bytes, needs {nbytes}")
+        return ctypes.c_void_p(workspace.data_ptr()), have
+    if nbytes == 0:
+        return None, 0
+    if stream is not None and not isinstance(stream, torch.cuda.Stream):
+        raise ValueError(f"{func}: pass a workspace tensor when the stream is a raw handle")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        ws.record_stream(stream)  # not reused by torch before the call's work on `stream` ends
+    return ctypes.c_void_p(ws.data_ptr()), nbytes
+
+
+def calibrate_workspace_bytes(shape: RrpShape, n_tokens: int, with_q: bool = True) -> int:
+    """Device workspace bytes of one calibrate_angles call (rrp_calibrate_angles_workspace_size)."""
+    return _abi.workspace_size("rrp_calibrate_angles", shape, int(n_tokens), 1 if with_q else 0)
+
+
+def quant_error_stats_workspace_bytes(shape: RrpShape, n_tokens: int) -> int:
+    """Device workspace bytes of one quant_error_stats call."""
+    return _abi.workspace_size("rrp_quant_error_stats", shape, int(n_tokens))
+
+
+def quant_error_sweep_workspace_bytes(shape: RrpShape, n_tokens: int) -> int:
+    """Device workspace bytes of one quant_error_sweep call."""
+    return _abi.workspace_size("rrp_quant_error_sweep", shape, int(n_tokens))
+
+
 def new_kv4_cache(n_slots: int, n_kv_heads: int, head_dim: int, group: int, device="cuda"):
     """Allocate one empty half (K or V) of a KV4 cache: packed codes uint8
     [n_slots][Hkv][d/2] and fp16 scales [n_slots][Hkv][d/group]."""
@@ -144,37 +179,45 @@ def rotate_quantize_qkv(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Ten
 
 def calibrate_angles(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor, pos: torch.Tensor, *,
                      moments: torch.Tensor, estimator="default", angles_out: Optional[torch.Tensor] = None,
-                     stream=None) -> None:
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Enqueue rrp_calibrate_angles: accumulate pair moments into `moments` and,
-    if angles_out is given, finalise the shared angles (see include/rrp.h)."""
+    if angles_out is given, finalise the shared angles (see include/rrp.h).
+    workspace: optional device tensor of at least calibrate_workspace_bytes()
+    bytes; by default one is taken from torch's caching allocator."""
     L = _abi.load()
     est = ESTIMATORS[estimator] if isinstance(estimator, str) else int(estimator)
     d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
     T = int(pos.numel())
     dt, dev = k.dtype, k.device
+    ws, ws_bytes = _workspace("rrp_calibrate_angles", calibrate_workspace_bytes(shape, T, q is not None), workspace,
+                              stream, dev)
     args = [
         ctypes.byref(shape), _dtype_code(k),
         _dev(q, "q", T * hq * d, dt, dev), _dev(k, "k", T * hk * d, dt, dev),
         _dev(pos, "pos", T, torch.int32, dev), T, est,
         _dev(moments, "moments", angle_sets(shape) * (d // 2) * 12, torch.float64, dev),
         _dev(angles_out, "angles_out", angle_sets(shape) * (d // 2), torch.float32, dev),
-        _stream_ptr(stream, dev),
+        ws, ws_bytes, _stream_ptr(stream, dev),
     ]
     _abi.check("rrp_calibrate_angles", L.rrp_calibrate_angles(*args))
 
 
 def quant_error_stats(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, support_b: int, group: int,
-                      stats_out: torch.Tensor, angles: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Enqueue rrp_quant_error_stats into stats_out (double[8], see include/rrp.h)."""
+                      stats_out: torch.Tensor, angles: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue rrp_quant_error_stats into stats_out (double[8], see include/rrp.h).
+    workspace: as for calibrate_angles (quant_error_stats_workspace_bytes())."""
     L = _abi.load()
     d, hk = shape.head_dim, shape.n_kv_heads
     T = int(pos.numel())
     dt, dev = k.dtype, k.device
+    ws, ws_bytes = _workspace("rrp_quant_error_stats", quant_error_stats_workspace_bytes(shape, T), workspace,
+                              stream, dev)
     args = [
         ctypes.byref(shape), _dtype_code(k), _dev(k, "k", T * hk * d, dt, dev),
         _dev(pos, "pos", T, torch.int32, dev), T,
         _dev(angles, "angles", angle_sets(shape) * (d // 2), torch.float32, dev), int(support_b), int(group),
-        _dev(stats_out, "stats_out", 8, torch.float64, dev), _stream_ptr(stream, dev),
+        _dev(stats_out, "stats_out", 8, torch.float64, dev), ws, ws_bytes, _stream_ptr(stream, dev),
     ]
     _abi.check("rrp_quant_error_stats", L.rrp_quant_error_stats(*args))
 
@@ -189,19 +232,24 @@ def sweep_supports(head_dim: int):
 
 
 def quant_error_sweep(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, group: int, stats_out: torch.Tensor,
-                      angles: Optional[torch.Tensor] = None, stream=None) -> None:
+                      angles: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
     """Enqueue rrp_quant_error_sweep: the statistics of quant_error_stats for every
     support b = 1, 2, 4, ..., head_dim into stats_out double[len(supports)][8]
-    (see include/rrp.h)."""
+    (see include/rrp.h).  workspace: as for calibrate_angles
+    (quant_error_sweep_workspace_bytes())."""
     L = _abi.load()
     d, hk = shape.head_dim, shape.n_kv_heads
     T = int(pos.numel())
     dt, dev = k.dtype, k.device
+    ws, ws_bytes = _workspace("rrp_quant_error_sweep", quant_error_sweep_workspace_bytes(shape, T), workspace,
+                              stream, dev)
     args = [
         ctypes.byref(shape), _dtype_code(k), _dev(k, "k", T * hk * d, dt, dev),
         _dev(pos, "pos", T, torch.int32, dev), T,
         _dev(angles, "angles", angle_sets(shape) * (d // 2), torch.float32, dev), int(group),
-        _dev(stats_out, "stats_out", 8 * len(sweep_supports(d)), torch.float64, dev), _stream_ptr(stream, dev),
+        _dev(stats_out, "stats_out", 8 * len(sweep_supports(d)), torch.float64, dev), ws, ws_bytes,
+        _stream_ptr(stream, dev),
     ]
     _abi.check("rrp_quant_error_sweep", L.rrp_quant_error_sweep(*args))
 
@@ -229,6 +277,8 @@ def decode_scores(shape: RrpShape, q: torch.Tensor, k_codes: torch.Tensor, k_sca
     _abi.check("rrp_decode_scores", L.rrp_decode_scores(*args))
 
 
-__all__ = ["layer_shape", "angle_sets", "decode_scores", "quant_error_sweep", "sweep_supports", "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
-           "new_moments", "RrpError", "RrpShape", "ESTIMATORS", "RRP_F32", "RRP_BF16",
-           "RRP_ROPE_HALF_SPLIT", "RRP_ROPE_INTERLEAVED"]
+__all__ = ["layer_shape", "angle_sets", "calibrate_workspace_bytes", "quant_error_stats_workspace_bytes",
+           "quant_error_sweep_workspace_bytes", "decode_scores", "quant_error_sweep", "sweep_supports",
+           "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
+           "new_moments", "RrpError", "RrpShape", "ESTIMATORS", "RRP_F32", "RRP_BF16", "RRP_ROPE_HALF_SPLIT",
+           "RRP_ROPE_INTERLEAVED"]

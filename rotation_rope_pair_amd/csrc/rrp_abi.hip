@@ -1,10 +1,12 @@
 // rrp_abi.hip -- the C-ABI entry points (include/rrp.h): host-side validation,
-// RoPE frequency table, stream-ordered scratch and kernel dispatch.
+// RoPE frequency table, workspace sizing and kernel dispatch.
 //
 // Every check runs before anything is enqueued, so an error return leaves the
 // stream untouched.  The RoPE frequencies are evaluated here on the host in
 // fp64 (libm pow) and rounded once to fp32; they travel to the kernels inside
-// the kernel argument block.
+// the kernel argument block.  The library allocates no memory: the block
+// partial sums of calibration and diagnostics live in a workspace the caller
+// passes in (its size comes from the *_workspace_size queries).
 #include <math.h>
 #include <stdint.h>
 
@@ -50,18 +52,36 @@ void fill_inv_freq(const rrp_shape* s, float* out) {
         out[k] = k < s->head_dim / 2 ? (float)pow(s->rope_theta, -2.0 * (double)k / (double)s->head_dim) : 0.0f;
 }
 
-// Stream-ordered scratch that is released on the same stream after use.
-struct Scratch {
-    void* p = nullptr;
-    hipStream_t st = nullptr;
-    hipError_t alloc(size_t bytes, hipStream_t stream) {
-        st = stream;
-        return hipMallocAsync(&p, bytes, stream);
-    }
-    ~Scratch() {
-        if (p) (void)hipFreeAsync(p, st);
-    }
-};
+// Workspace bytes of one calibration call: the block partials [P * 5][blocks]
+// (0 when there are no tokens).  with_q: the Q stream is accumulated.
+size_t calib_workspace_bytes(const rrp_shape* s, int64_t n_tokens, bool with_q) {
+    if (n_tokens <= 0) return 0;
+    int nbq = 0, nbk = 0;
+    const int nb = rrp::calib_blocks(n_tokens, with_q && s->n_q_heads > 0, s->n_q_heads, s->n_kv_heads,
+                                     s->head_dim, angle_sets(s), &nbq, &nbk);
+    return (size_t)nb * (size_t)(s->head_dim / 2) * 5 * sizeof(double);
+}
+
+// Supports reduced by the diagnostics: 1, or every b = 1, 2, ..., head_dim (sweep).
+int stats_supports(const rrp_shape* s, bool sweep) {
+    int n = 1;
+    if (sweep)
+        for (int b = 1; b < s->head_dim; b <<= 1) ++n;
+    return n;
+}
+
+// Workspace bytes of one diagnostics call: the block partials [supports * 5][blocks].
+size_t stats_workspace_bytes(const rrp_shape* s, int64_t n_tokens, bool sweep) {
+    if (n_tokens <= 0) return 0;
+    return (size_t)rrp::stats_blocks(n_tokens) * (size_t)stats_supports(s, sweep) * 5 * sizeof(double);
+}
+
+// A workspace of `have` bytes at `p` for a call needing `need` bytes.
+int check_workspace(const void* p, size_t have, size_t need) {
+    if (need == 0) return RRP_OK;
+    if (p == nullptr || have < need) return RRP_ERR_INVALID_ARG;
+    return aligned(p, 8) ? RRP_OK : RRP_ERR_MISALIGNED;
+}
 
 }  // namespace
 
@@ -160,38 +180,39 @@ RRP_EXPORT int rrp_rotate_quantize_qkv(const rrp_shape* shape, int32_t dtype, co
                            v_rot_f32, v_scale_f32, stream);
 }
 
-RRP_EXPORT int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
-                                    const int32_t* pos, int64_t n_tokens, int32_t estimator,
-                                    double* moments, float* angles_out, void* stream) {
-    int st = check_shape(shape, dtype);
+RRP_EXPORT int rrp_calibrate_angles_workspace_size(const rrp_shape* shape, int64_t n_tokens, int32_t with_q,
+                                                   size_t* bytes) {
+    const int st = check_shape(shape, RRP_BF16);
     if (st != RRP_OK) return st;
-    if (estimator < RRP_EST_DEFAULT || estimator > RRP_EST_STREAM_BALANCED) return RRP_ERR_INVALID_ARG;
-    if (n_tokens < 0 || moments == nullptr) return RRP_ERR_INVALID_ARG;
-    if (n_tokens > 0 && (k == nullptr || pos == nullptr)) return RRP_ERR_INVALID_ARG;
-    if (q == nullptr && estimator != RRP_EST_K_ONLY && n_tokens > 0) return RRP_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(pos, 4) || !aligned(moments, 8) || !aligned(angles_out, 4))
-        return RRP_ERR_MISALIGNED;
-    const hipStream_t s = (hipStream_t)stream;
-    const int P = shape->head_dim / 2;
+    if (n_tokens < 0 || bytes == nullptr) return RRP_ERR_INVALID_ARG;
+    *bytes = calib_workspace_bytes(shape, n_tokens, with_q != 0);
+    return RRP_OK;
+}
 
+namespace {
+
+// Body of rrp_calibrate_angles, with the block partials in `partials`
+// (calib_workspace_bytes of them; checked by the caller).
+int calibrate(const rrp_shape* shape, int32_t dtype, const void* q, const void* k, const int32_t* pos,
+              int64_t n_tokens, int32_t estimator, double* moments, float* angles_out, double* partials,
+              hipStream_t s) {
+    const int P = shape->head_dim / 2;
     rrp::CalibFinalArgs f{};
     f.moments = moments;
     f.angles_out = angles_out;
     f.n_pairs = P;
     f.n_sets = angle_sets(shape);
     f.estimator = estimator;
-    Scratch scratch;
     if (n_tokens > 0) {
         int nbq = 0, nbk = 0;
         const bool with_q = q != nullptr && shape->n_q_heads > 0;
-        const int nb = rrp::calib_blocks(n_tokens, with_q, shape->n_q_heads, shape->n_kv_heads, shape->head_dim, f.n_sets,
-                                         &nbq, &nbk);
-        if (scratch.alloc((size_t)nb * P * 5 * sizeof(double), s) != hipSuccess) return RRP_ERR_HIP;
+        rrp::calib_blocks(n_tokens, with_q, shape->n_q_heads, shape->n_kv_heads, shape->head_dim, f.n_sets, &nbq,
+                          &nbk);
         rrp::CalibArgs a{};
         a.q = q;
         a.k = k;
         a.pos = pos;
-        a.partials = static_cast<double*>(scratch.p);
+        a.partials = partials;
         a.n_tokens = n_tokens;
         a.hq = shape->n_q_heads;
         a.hk = shape->n_kv_heads;
@@ -211,12 +232,41 @@ RRP_EXPORT int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const
     return rrp::launch_calibrate_final(f, s) == hipSuccess ? RRP_OK : RRP_ERR_HIP;
 }
 
+// Argument checks of rrp_calibrate_angles (everything but the workspace).
+int check_calibrate(const rrp_shape* shape, int32_t dtype, const void* q, const void* k, const int32_t* pos,
+                    int64_t n_tokens, int32_t estimator, const double* moments, const float* angles_out) {
+    int st = check_shape(shape, dtype);
+    if (st != RRP_OK) return st;
+    if (estimator < RRP_EST_DEFAULT || estimator > RRP_EST_STREAM_BALANCED) return RRP_ERR_INVALID_ARG;
+    if (n_tokens < 0 || moments == nullptr) return RRP_ERR_INVALID_ARG;
+    if (n_tokens > 0 && (k == nullptr || pos == nullptr)) return RRP_ERR_INVALID_ARG;
+    if (q == nullptr && estimator != RRP_EST_K_ONLY && n_tokens > 0) return RRP_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(pos, 4) || !aligned(moments, 8) || !aligned(angles_out, 4))
+        return RRP_ERR_MISALIGNED;
+    return RRP_OK;
+}
+
+}  // namespace
+
+RRP_EXPORT int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
+                                    const int32_t* pos, int64_t n_tokens, int32_t estimator,
+                                    double* moments, float* angles_out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    int st = check_calibrate(shape, dtype, q, k, pos, n_tokens, estimator, moments, angles_out);
+    if (st != RRP_OK) return st;
+    st = check_workspace(workspace, workspace_bytes, calib_workspace_bytes(shape, n_tokens, q != nullptr));
+    if (st != RRP_OK) return st;
+    return calibrate(shape, dtype, q, k, pos, n_tokens, estimator, moments, angles_out,
+                     static_cast<double*>(workspace), (hipStream_t)stream);
+}
+
 namespace {
 
 // Shared body of the single-support and sweep diagnostics (support_b is ignored
 // by the sweep, which covers b = 1, 2, 4, ..., head_dim).
 int quant_error(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos, int64_t n_tokens,
-                const float* angles, int32_t support_b, int32_t group, bool sweep, double* stats_out, void* stream) {
+                const float* angles, int32_t support_b, int32_t group, bool sweep, double* stats_out,
+                void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_shape(shape, dtype);
     if (st != RRP_OK) return st;
     if ((st = check_b_g(shape, sweep ? 1 : support_b, group)) != RRP_OK) return st;
@@ -224,25 +274,23 @@ int quant_error(const rrp_shape* shape, int32_t dtype, const void* k, const int3
     if (n_tokens > 0 && (k == nullptr || pos == nullptr)) return RRP_ERR_INVALID_ARG;
     if (!aligned(k, 16) || !aligned(pos, 4) || !aligned(angles, 4) || !aligned(stats_out, 8))
         return RRP_ERR_MISALIGNED;
+    if ((st = check_workspace(workspace, workspace_bytes, stats_workspace_bytes(shape, n_tokens, sweep))) != RRP_OK)
+        return st;
     const hipStream_t s = (hipStream_t)stream;
-    int n_sets = 1;
-    if (sweep)
-        for (int b = 1; b < shape->head_dim; b <<= 1) ++n_sets;
+    const int n_sets = stats_supports(shape, sweep);
     rrp::StatsFinalArgs f{};
     f.stats_out = stats_out;
     f.n_sets = n_sets;
     f.sweep = sweep ? 1 : 0;
     f.n_rows = (double)n_tokens * shape->n_kv_heads;
     f.n_groups = f.n_rows * (shape->head_dim / group);
-    Scratch scratch;
     if (n_tokens > 0) {
         const int nb = rrp::stats_blocks(n_tokens);
-        if (scratch.alloc((size_t)nb * n_sets * 5 * sizeof(double), s) != hipSuccess) return RRP_ERR_HIP;
         rrp::StatsArgs a{};
         a.k = k;
         a.pos = pos;
         a.angles = angles;
-        a.partials = static_cast<double*>(scratch.p);
+        a.partials = static_cast<double*>(workspace);
         a.n_tokens = n_tokens;
         a.hk = shape->n_kv_heads;
         a.support_b = sweep ? 1 : support_b;
@@ -260,16 +308,34 @@ int quant_error(const rrp_shape* shape, int32_t dtype, const void* k, const int3
 
 }  // namespace
 
+RRP_EXPORT int rrp_quant_error_stats_workspace_size(const rrp_shape* shape, int64_t n_tokens, size_t* bytes) {
+    const int st = check_shape(shape, RRP_BF16);
+    if (st != RRP_OK) return st;
+    if (n_tokens < 0 || bytes == nullptr) return RRP_ERR_INVALID_ARG;
+    *bytes = stats_workspace_bytes(shape, n_tokens, false);
+    return RRP_OK;
+}
+
+RRP_EXPORT int rrp_quant_error_sweep_workspace_size(const rrp_shape* shape, int64_t n_tokens, size_t* bytes) {
+    const int st = check_shape(shape, RRP_BF16);
+    if (st != RRP_OK) return st;
+    if (n_tokens < 0 || bytes == nullptr) return RRP_ERR_INVALID_ARG;
+    *bytes = stats_workspace_bytes(shape, n_tokens, true);
+    return RRP_OK;
+}
+
 RRP_EXPORT int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
                                      int64_t n_tokens, const float* angles, int32_t support_b, int32_t group,
-                                     double* stats_out, void* stream) {
-    return quant_error(shape, dtype, k, pos, n_tokens, angles, support_b, group, false, stats_out, stream);
+                                     double* stats_out, void* workspace, size_t workspace_bytes, void* stream) {
+    return quant_error(shape, dtype, k, pos, n_tokens, angles, support_b, group, false, stats_out, workspace,
+                       workspace_bytes, stream);
 }
 
 RRP_EXPORT int rrp_quant_error_sweep(const rrp_shape* shape, int32_t dtype, const void* k, const int32_t* pos,
                                      int64_t n_tokens, const float* angles, int32_t group, double* stats_out,
-                                     void* stream) {
-    return quant_error(shape, dtype, k, pos, n_tokens, angles, 1, group, true, stats_out, stream);
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    return quant_error(shape, dtype, k, pos, n_tokens, angles, 1, group, true, stats_out, workspace,
+                       workspace_bytes, stream);
 }
 
 RRP_EXPORT int rrp_decode_scores(const rrp_shape* shape, int32_t dtype, const void* q, int64_t n_seqs,

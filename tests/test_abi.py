@@ -27,8 +27,10 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["rrp_calibrate_angles", "rrp_quant_error_stats", "rrp_rotate_quantize_qk",
-                                           "rrp_rotate_quantize_qkv", "rrp_decode_scores", "rrp_quant_error_sweep",
+    assert declared_functions() == sorted(["rrp_calibrate_angles", "rrp_calibrate_angles_workspace_size",
+                                           "rrp_quant_error_stats", "rrp_quant_error_stats_workspace_size",
+                                           "rrp_rotate_quantize_qk", "rrp_rotate_quantize_qkv", "rrp_decode_scores",
+                                           "rrp_quant_error_sweep", "rrp_quant_error_sweep_workspace_size",
                                            "rrp_status_string", "rrp_version"])
 
 
@@ -93,9 +95,10 @@ def test_angle_heads_validation(lib):
     assert rot(lib, shape=_shape(ah=4)) == 1                      # neither shared nor n_kv_heads
     assert rot(lib, shape=_shape(hq=12, hk=8, ah=8)) == 1         # query heads must split evenly
     assert rot(lib, shape=_shape(hq=32, hk=16, ah=16)) == 3       # more sets than the LDS tables hold
-    assert lib.rrp_calibrate_angles(ctypes.byref(_shape(ah=3)), 1, P16, P16, P16, 4, 0, P16, None, None) == 1
-    assert lib.rrp_quant_error_stats(ctypes.byref(_shape(ah=2)), 1, P16, P16, 4, None, 128, 128, P16,
-                                     None) == 1
+    assert lib.rrp_calibrate_angles(ctypes.byref(_shape(ah=3)), 1, P16, P16, P16, 4, 0, P16, None, P16, 1 << 30,
+                                    None) == 1
+    assert lib.rrp_quant_error_stats(ctypes.byref(_shape(ah=2)), 1, P16, P16, 4, None, 128, 128, P16, P16,
+                                     1 << 30, None) == 1
     from rotation_rope_pair_amd import api
     assert api.angle_sets(api.layer_shape(32, 8, 128, 5e5)) == 1
     assert api.angle_sets(api.layer_shape(32, 8, 128, 5e5, angle_heads=1)) == 1
@@ -132,31 +135,77 @@ def test_decode_scores_validation(lib):
     assert dec(shape=_shape(d=96)) == 3
 
 
+BIG = 1 << 30  # a workspace size above any requirement
+
+
+def ws_size(lib, func, shape, *args):
+    out = ctypes.c_size_t(0)
+    rc = getattr(lib, func + "_workspace_size")(ctypes.byref(shape), *args, ctypes.byref(out))
+    return rc, out.value
+
+
 def test_calibrate_validation(lib):
-    def cal(shape=None, dtype=1, q=P16, k=P16, pos=P16, T=4, est=0, mom=P16, ang=None):
-        return lib.rrp_calibrate_angles(ctypes.byref(shape or _shape()), dtype, q, k, pos, T, est, mom, ang, None)
+    def cal(shape=None, dtype=1, q=P16, k=P16, pos=P16, T=4, est=0, mom=P16, ang=None, ws=P16, ws_bytes=BIG):
+        return lib.rrp_calibrate_angles(ctypes.byref(shape or _shape()), dtype, q, k, pos, T, est, mom, ang, ws,
+                                        ws_bytes, None)
     assert cal(est=3) == 1 and cal(est=-1) == 1
     assert cal(mom=None) == 1
     assert cal(q=None, est=0) == 1 and cal(q=None, est=2) == 1    # Q needed by these estimators
     assert cal(k=None) == 1 and cal(pos=None) == 1 and cal(T=-2) == 1
     assert cal(shape=_shape(d=256)) == 3
     assert cal(k=P2) == 2 and cal(mom=ctypes.c_void_p((1 << 20) + 4)) == 2
-    assert cal(T=0, q=None, k=None, pos=None, ang=None) == 0      # nothing to do
+    assert cal(T=0, q=None, k=None, pos=None, ang=None, ws=None, ws_bytes=0) == 0  # nothing to do
+
+
+def test_calibrate_workspace(lib):
+    """The size query, and a missing, short or misaligned workspace rejected
+    before anything is enqueued."""
+    def cal(ws=P16, ws_bytes=BIG, q=P16, est=0, T=4096):
+        return lib.rrp_calibrate_angles(ctypes.byref(_shape()), 1, q, P16, P16, T, est, P16, None, ws, ws_bytes,
+                                        None)
+    rc, need = ws_size(lib, "rrp_calibrate_angles", _shape(), 4096, 1)
+    assert rc == 0 and need > 0 and need % (64 * 5 * 8) == 0      # [blocks][pairs][5 sums] doubles
+    assert need <= 4096 * 64 * 5 * 8
+    rc, need_k = ws_size(lib, "rrp_calibrate_angles", _shape(), 4096, 0)
+    assert rc == 0 and 0 < need_k <= need                         # K stream only: no more blocks
+    assert ws_size(lib, "rrp_calibrate_angles", _shape(), 0, 1) == (0, 0)
+    _, big = ws_size(lib, "rrp_calibrate_angles", _shape(), 1 << 40, 1)
+    assert big == 4096 * 64 * 5 * 8                               # capped partial columns
+    _, sets = ws_size(lib, "rrp_calibrate_angles", _shape(ah=8), 1 << 40, 1)
+    assert sets <= 4096 * 64 * 5 * 8
+    assert ws_size(lib, "rrp_calibrate_angles", _shape(d=96), 16, 1)[0] == 3
+    assert ws_size(lib, "rrp_calibrate_angles", _shape(), -1, 1)[0] == 1
+    assert lib.rrp_calibrate_angles_workspace_size(ctypes.byref(_shape()), 16, 1, None) == 1
+    assert cal(ws=None) == 1 and cal(ws_bytes=need - 8) == 1
+    assert cal(q=None, est=1, ws_bytes=need_k - 8) == 1
+    assert cal(ws=ctypes.c_void_p((1 << 20) + 4)) == 2
 
 
 def test_stats_validation(lib):
-    def stt(T=4, k=P16, pos=P16, b=128, g=128, out=P16):
-        return lib.rrp_quant_error_stats(ctypes.byref(_shape()), 1, k, pos, T, None, b, g, out, None)
+    def stt(T=4, k=P16, pos=P16, b=128, g=128, out=P16, ws=P16, ws_bytes=BIG):
+        return lib.rrp_quant_error_stats(ctypes.byref(_shape()), 1, k, pos, T, None, b, g, out, ws, ws_bytes, None)
     assert stt(out=None) == 1 and stt(k=None) == 1 and stt(b=5) == 1 and stt(g=3) == 1
     assert stt(out=ctypes.c_void_p((1 << 20) + 4)) == 2
+    rc, need = ws_size(lib, "rrp_quant_error_stats", _shape(), 131072)
+    assert rc == 0 and 0 < need <= 4096 * 5 * 8
+    assert ws_size(lib, "rrp_quant_error_stats", _shape(), 0) == (0, 0)
+    assert stt(T=131072, ws=None) == 1 and stt(T=131072, ws_bytes=need - 1) == 1
+    assert stt(T=131072, ws=ctypes.c_void_p((1 << 20) + 4)) == 2
 
 
 def test_sweep_validation(lib):
-    def swp(T=4, k=P16, pos=P16, g=128, out=P16, shape=None):
-        return lib.rrp_quant_error_sweep(ctypes.byref(shape or _shape()), 1, k, pos, T, None, g, out, None)
+    def swp(T=4, k=P16, pos=P16, g=128, out=P16, shape=None, ws=P16, ws_bytes=BIG):
+        return lib.rrp_quant_error_sweep(ctypes.byref(shape or _shape()), 1, k, pos, T, None, g, out, ws, ws_bytes,
+                                         None)
     assert swp(out=None) == 1 and swp(k=None) == 1 and swp(g=3) == 1 and swp(g=256) == 1 and swp(T=-1) == 1
     assert swp(out=ctypes.c_void_p((1 << 20) + 4)) == 2 and swp(k=P2) == 2
     assert swp(shape=_shape(d=96)) == 3
+    rc, need = ws_size(lib, "rrp_quant_error_sweep", _shape(), 131072)
+    _, one = ws_size(lib, "rrp_quant_error_stats", _shape(), 131072)
+    assert rc == 0 and need == 8 * one                            # b = 1, 2, ..., 128: eight supports
+    _, need64 = ws_size(lib, "rrp_quant_error_sweep", _shape(d=64), 131072)
+    assert need64 == 7 * one
+    assert swp(T=131072, ws_bytes=need - 8) == 1
 
 
 def test_binding_rejects_host_tensors_before_any_launch():

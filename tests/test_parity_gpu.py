@@ -850,3 +850,39 @@ def test_grid_stride_prefill_128k_with_v(b, g, ah):
     out = run_rotate_qkv(w, inp, ang, b, g, debug=False, ah=ah)
     idx = grid_sample(w.n_tokens, 512, 2500 + b)
     print(b, g, ah, check_rotate(w, inp, out, ang, b, g, idx, ah=ah), check_v(w, inp, out, g, idx))
+
+
+# ---------------------------------------------------------------------------
+# caller-owned workspace
+# ---------------------------------------------------------------------------
+
+def test_explicit_workspace_reused_across_calls():
+    """One oversized workspace tensor passed to calibration, diagnostics and the
+    sweep, call after call, gives the same results as the binding's own
+    per-call workspace; a short one is rejected before any launch."""
+    w, inp = W.WORKLOADS[3], inputs(3)
+    shape = shape_of(w)
+    q, k, pos = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["pos"])
+    T = w.n_tokens
+    need = max(rrp.calibrate_workspace_bytes(shape, T), rrp.quant_error_stats_workspace_bytes(shape, T),
+               rrp.quant_error_sweep_workspace_bytes(shape, T))
+    ws = torch.full((need + 4096,), 0xA5, dtype=torch.uint8, device=DEV)  # stale contents must not matter
+    nb = len(rrp.sweep_supports(w.head_dim))
+    results = []
+    for workspace in (ws, None, ws):
+        mom = rrp.new_moments(w.head_dim, DEV)
+        ang = torch.empty(w.n_pairs, dtype=torch.float32, device=DEV)
+        rrp.calibrate_angles(shape, q, k, pos, moments=mom, angles_out=ang, workspace=workspace)
+        st = torch.empty(8, dtype=torch.float64, device=DEV)
+        rrp.quant_error_stats(shape, k, pos, support_b=16, group=32, stats_out=st, angles=ang, workspace=workspace)
+        sw = torch.empty((nb, 8), dtype=torch.float64, device=DEV)
+        rrp.quant_error_sweep(shape, k, pos, group=128, stats_out=sw, angles=ang, workspace=workspace)
+        torch.cuda.synchronize()
+        results.append([x.cpu().numpy() for x in (mom, ang, st, sw)])
+    for a, b in zip(results[0], results[1]):
+        assert np.array_equal(a, b)
+    for a, b in zip(results[0], results[2]):
+        assert np.array_equal(a, b)
+    short = torch.empty(rrp.calibrate_workspace_bytes(shape, T) - 8, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError, match="workspace"):
+        rrp.calibrate_angles(shape, q, k, pos, moments=rrp.new_moments(w.head_dim, DEV), workspace=short)

@@ -200,6 +200,26 @@ int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const void* q, c
                          double* moments, float* angles_out, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* rrp_calibrate_angles_noalloc -- rrp_calibrate_angles for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation and results (the same
+ * block partials, reduced in the same order), with the partials in a static
+ * device array of the library instead of a caller workspace.  That array holds
+ * 4096 * 64 * 5 doubles (10 MiB, the largest calibration workspace of any
+ * accepted shape); each GPU the library runs on holds its own copy until the
+ * process ends.  A call whose workspace size would exceed it returns
+ * RRP_ERR_UNSUPPORTED (no accepted shape does).  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or different host threads without ordering)
+ * race and give wrong moments; calls ordered on one stream are safe.  The
+ * first call on a device looks up the array's device address (no allocation).
+ * Arguments, outputs and errors as rrp_calibrate_angles, without the
+ * workspace; RRP_ERR_HIP also reports a failed lookup of the stream's device or
+ * of the array. */
+int rrp_calibrate_angles_noalloc(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
+                                 const int32_t* pos, int64_t n_tokens, int32_t estimator, double* moments,
+                                 float* angles_out, void* stream);
+
 /* rrp_quant_error_stats -- the diagnostic pass ("contributions" and "results"
  * sections: K range and relative quantisation error along the block-Hadamard
  * support interpolation).  Transforms every K row as rrp_rotate_quantize_qk

@@ -17,7 +17,7 @@ RRP_ROPE_HALF_SPLIT, RRP_ROPE_INTERLEAVED = 0, 1
 
 # Symbols declared in include/rrp.h.
 EXPORTS = ("rrp_rotate_quantize_qk", "rrp_rotate_quantize_qkv", "rrp_calibrate_angles",
-           "rrp_calibrate_angles_workspace_size", "rrp_quant_error_stats", "rrp_quant_error_stats_workspace_size",
+           "rrp_calibrate_angles_noalloc", "rrp_calibrate_angles_workspace_size", "rrp_quant_error_stats", "rrp_quant_error_stats_workspace_size",
            "rrp_quant_error_sweep", "rrp_quant_error_sweep_workspace_size", "rrp_decode_scores",
            "rrp_status_string", "rrp_version")
 
@@ -60,6 +60,7 @@ def load():
                                           i64, vp, vp, vp, vp, vp, vp]
     L.rrp_calibrate_angles.argtypes = [sp, i32, vp, vp, vp, i64, i32, vp, vp, vp, sz, vp]
     L.rrp_calibrate_angles_workspace_size.argtypes = [sp, i64, i32, szp]
+    L.rrp_calibrate_angles_noalloc.argtypes = [sp, i32, vp, vp, vp, i64, i32, vp, vp, vp]
     L.rrp_quant_error_sweep.argtypes = [sp, i32, vp, vp, i64, vp, i32, vp, vp, sz, vp]
     L.rrp_quant_error_sweep_workspace_size.argtypes = [sp, i64, szp]
     L.rrp_decode_scores.argtypes = [sp, i32, vp, i64, vp, vp, i32, i64, vp, vp, i32, vp, vp]

@@ -202,6 +202,28 @@ def calibrate_angles(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor
     _abi.check("rrp_calibrate_angles", L.rrp_calibrate_angles(*args))
 
 
+def calibrate_angles_noalloc(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor, pos: torch.Tensor, *,
+                             moments: torch.Tensor, estimator="default", angles_out: Optional[torch.Tensor] = None,
+                             stream=None) -> None:
+    """Enqueue rrp_calibrate_angles_noalloc: calibrate_angles with no device
+    allocation at all (the library's static scratch holds the partials).  Calls
+    that overlap on one GPU race (see include/rrp.h)."""
+    L = _abi.load()
+    est = ESTIMATORS[estimator] if isinstance(estimator, str) else int(estimator)
+    d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
+    T = int(pos.numel())
+    dt, dev = k.dtype, k.device
+    args = [
+        ctypes.byref(shape), _dtype_code(k),
+        _dev(q, "q", T * hq * d, dt, dev), _dev(k, "k", T * hk * d, dt, dev),
+        _dev(pos, "pos", T, torch.int32, dev), T, est,
+        _dev(moments, "moments", angle_sets(shape) * (d // 2) * 12, torch.float64, dev),
+        _dev(angles_out, "angles_out", angle_sets(shape) * (d // 2), torch.float32, dev),
+        _stream_ptr(stream, dev),
+    ]
+    _abi.check("rrp_calibrate_angles_noalloc", L.rrp_calibrate_angles_noalloc(*args))
+
+
 def quant_error_stats(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, support_b: int, group: int,
                       stats_out: torch.Tensor, angles: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -277,7 +299,7 @@ def decode_scores(shape: RrpShape, q: torch.Tensor, k_codes: torch.Tensor, k_sca
     _abi.check("rrp_decode_scores", L.rrp_decode_scores(*args))
 
 
-__all__ = ["layer_shape", "angle_sets", "calibrate_workspace_bytes", "quant_error_stats_workspace_bytes",
+__all__ = ["layer_shape", "angle_sets", "calibrate_angles_noalloc", "calibrate_workspace_bytes", "quant_error_stats_workspace_bytes",
            "quant_error_sweep_workspace_bytes", "decode_scores", "quant_error_sweep", "sweep_supports",
            "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
            "new_moments", "RrpError", "RrpShape", "ESTIMATORS", "RRP_F32", "RRP_BF16", "RRP_ROPE_HALF_SPLIT",

@@ -10,6 +10,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "rrp.h"
@@ -258,6 +260,70 @@ RRP_EXPORT int rrp_calibrate_angles(const rrp_shape* shape, int32_t dtype, const
     if (st != RRP_OK) return st;
     return calibrate(shape, dtype, q, k, pos, n_tokens, estimator, moments, angles_out,
                      static_cast<double*>(workspace), (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// rrp_calibrate_angles_noalloc: the calibration with its block partials in a
+// static device array of this library instead of a caller workspace, for
+// callers that cannot allocate.  The array is sized for the largest workspace
+// of any accepted shape (kMaxCalibBlocks partial columns of 64 pairs x 5 sums:
+// 10 MiB), so no accepted call exceeds it.  Every partial a call reads is
+// written earlier by the same call, so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kStaticScratchDoubles = (size_t)rrp::kMaxCalibBlocks * rrp::kMaxPairs * 5;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) double scratch[kStaticScratchDoubles];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+double* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device (null until looked up)
+
+// The device address of `scratch` on `device`: looked up once per device, with
+// that device current (each device holds its own copy of the array).
+hipError_t static_scratch(int device, double** out) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[device] == nullptr) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != device) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[device] = static_cast<double*>(p);
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
+
+}  // namespace
+
+RRP_EXPORT int rrp_calibrate_angles_noalloc(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
+                                            const int32_t* pos, int64_t n_tokens, int32_t estimator,
+                                            double* moments, float* angles_out, void* stream) {
+    int st = check_calibrate(shape, dtype, q, k, pos, n_tokens, estimator, moments, angles_out);
+    if (st != RRP_OK) return st;
+    const size_t need = calib_workspace_bytes(shape, n_tokens, q != nullptr);
+    if (need > sizeof(scratch)) return RRP_ERR_UNSUPPORTED;  // beyond the static scratch (no accepted shape)
+    double* partials = nullptr;
+    if (need > 0) {
+        int device = -1;
+        hipError_t e = stream != nullptr ? hipStreamGetDevice((hipStream_t)stream, &device) : hipGetDevice(&device);
+        if (e == hipSuccess) e = static_scratch(device, &partials);
+        if (e != hipSuccess) return RRP_ERR_HIP;
+    }
+    return calibrate(shape, dtype, q, k, pos, n_tokens, estimator, moments, angles_out, partials,
+                     (hipStream_t)stream);
 }
 
 namespace {

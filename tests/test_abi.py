@@ -27,7 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["rrp_calibrate_angles", "rrp_calibrate_angles_workspace_size",
+    assert declared_functions() == sorted(["rrp_calibrate_angles", "rrp_calibrate_angles_noalloc",
+                                           "rrp_calibrate_angles_workspace_size",
                                            "rrp_quant_error_stats", "rrp_quant_error_stats_workspace_size",
                                            "rrp_rotate_quantize_qk", "rrp_rotate_quantize_qkv", "rrp_decode_scores",
                                            "rrp_quant_error_sweep", "rrp_quant_error_sweep_workspace_size",
@@ -179,6 +180,17 @@ def test_calibrate_workspace(lib):
     assert cal(ws=None) == 1 and cal(ws_bytes=need - 8) == 1
     assert cal(q=None, est=1, ws_bytes=need_k - 8) == 1
     assert cal(ws=ctypes.c_void_p((1 << 20) + 4)) == 2
+
+
+def test_calibrate_noalloc_validation(lib):
+    """The no-allocation variant checks its arguments exactly as rrp_calibrate_angles
+    does, before touching any device."""
+    def cal(shape=None, dtype=1, q=P16, k=P16, pos=P16, T=4, est=0, mom=P16, ang=None):
+        return lib.rrp_calibrate_angles_noalloc(ctypes.byref(shape or _shape()), dtype, q, k, pos, T, est, mom, ang,
+                                                None)
+    assert cal(est=3) == 1 and cal(mom=None) == 1 and cal(q=None, est=0) == 1 and cal(k=None) == 1
+    assert cal(T=-1) == 1 and cal(shape=_shape(d=256)) == 3 and cal(shape=_shape(ah=3)) == 1
+    assert cal(k=P2) == 2 and cal(mom=ctypes.c_void_p((1 << 20) + 4)) == 2
 
 
 def test_stats_validation(lib):

@@ -1,6 +1,6 @@
 // rrp_stats.hip -- diagnostic pass: K range and quantisation error of the
 // transformed K rows at one support b, or at every support b = 1 .. head_dim
-// from one read of K (the support sweep).
+// in one call (the support sweep: kSweepParts launches, each reading K once).
 //
 // Every K row goes through exactly the fp64 K transform and quantiser of the
 // hot path (same device functions), is dequantised with its stored fp16
@@ -224,8 +224,9 @@ __global__ __launch_bounds__(256) void stats_kernel(const StatsArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Support sweep: the statistics of every support b = 1, 2, 4, ..., D from two
-// reads of K (one per half of the supports).  Each row is rotated once (RoPE + R_phi, natural channel order),
+// Support sweep: the statistics of every support b = 1, 2, 4, ..., D from
+// kSweepParts reads of K (one launch per part of the supports).  Each row is
+// rotated once per launch (RoPE + R_phi, natural channel order),
 // its b = 1 statistics are taken, then the Walsh-Hadamard butterflies are
 // applied one channel bit at a time from the lowest, each followed by a factor
 // 1/sqrt(2): after the stage of bit j - 1 the row holds the normalised block

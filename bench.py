@@ -15,11 +15,12 @@ first few tens of launches of a process are slower) before the timed window,
 whatever --warmup says; the JSON line records that settle time and its launch
 count, and the per-launch median, min and max beside the mean.
 
---hot-path-only skips the supporting passes, the decode timing and the CPU
-baseline (short runs under a profiler).  Every run also times a plain
-device-to-device copy of the Q tensor (known size: 1 GiB read + 1 GiB written)
-as the practical streaming ceiling and as the reference kernel that scales the
-profiler's FETCH_SIZE / WRITE_SIZE counters.
+--hot-path-only skips the supporting passes, the per-workload timings, the
+decode timing and the CPU baseline (short runs under a profiler).  Every run
+also times torch's device-to-device copy of the Q tensor (known size: 1 GiB
+read + 1 GiB written; the reference kernel that scales the profiler's
+FETCH_SIZE / WRITE_SIZE counters) and the streaming-ceiling kernels of
+libstream_probe.so (copy, read-only and write-only at the same size).
 """
 import argparse
 import hashlib
@@ -265,6 +266,154 @@ def decode_scores_timing(dev, stream, reps=40):
             "decode_scores_hbm_gbs": nbytes / (ms * 1e-3) / 1e9}
 
 
+PROBE_LIB = os.path.join(ROOT, "rotation_rope_pair_amd", "libstream_probe.so")
+
+
+def stream_ceiling(src, dst, stream, reps=20):
+    """The GPU's practical streaming rates from plain kernels of known traffic
+    (rotation_rope_pair_amd/csrc/stream_probe.hip: 16-byte non-temporal
+    accesses, as in the rotate kernel): copy of the 1 GiB src into dst (1 GiB
+    read + 1 GiB written), read-only of src, write-only of dst."""
+    import ctypes
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        raise ImportError(f"{PROBE_LIB} is missing; run rotation_rope_pair_amd/build.py")
+    L = ctypes.CDLL(PROBE_LIB)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.stream_probe_copy.argtypes = [vp, vp, sz, vp]
+    L.stream_probe_read.argtypes = [vp, sz, vp, vp]
+    L.stream_probe_write.argtypes = [vp, sz, vp]
+    n = src.numel() * src.element_size()
+    sink = torch.zeros(4, dtype=torch.int32, device=src.device)
+    sp = vp(stream.cuda_stream)
+    runs = {"copy": (lambda: L.stream_probe_copy(vp(src.data_ptr()), vp(dst.data_ptr()), n, sp), 2 * n),
+            "read": (lambda: L.stream_probe_read(vp(src.data_ptr()), n, vp(sink.data_ptr()), sp), n),
+            "write": (lambda: L.stream_probe_write(vp(dst.data_ptr()), n, sp), n)}
+    out = {"kernels": "rotation_rope_pair_amd/csrc/stream_probe.hip", "bytes_per_buffer": n}
+    for name, (fn, nbytes) in runs.items():
+        if fn() != 0:
+            raise RuntimeError(f"stream_probe_{name} failed")
+        settle(fn, 0.3)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"{name}_ms"] = ms
+        out[f"{name}_GBs"] = nbytes / (ms * 1e-3) / 1e9
+    return out
+
+
+INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
+ROTATED_FOOTPRINT = 1 << 30        # bytes the rotated buffer sets of one config span at least
+
+
+def graph_us_per_launch(launches, stream, target_ms=50.0):
+    """GPU time per launch of the closures in `launches`, captured once into a HIP
+    graph (so no host launch cost sits between them) and replayed back to back
+    for about target_ms after an untimed settle."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # first launches outside the capture
+        for fn in launches:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for fn in launches:
+            fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_replay = max(e0.elapsed_time(e1), 1e-3)
+    settle(graph.replay, per_replay, 25.0)
+    replays = max(20, int(target_ms / per_replay))
+    e0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * len(launches))
+
+
+def per_config_timing(dev, stream, with_oracle):
+    """rotate_quantize_qk on each workload of the pages' shapes besides the 128K
+    prefill (the tiny fp32 reference, the 1B and 3B layers, the 256-token decode
+    batch): GPU time per launch over rotated buffer sets spanning at least 1 GiB
+    (so successive launches do not find their inputs in the 256 MB Infinity
+    Cache), through a HIP graph; tokens/s and algorithmic GB/s; and the CPU
+    oracle on the same inputs (every token)."""
+    import numpy as np
+    import torch
+    import rotation_rope_pair_amd as rrp
+    from rotation_rope_pair_amd import workloads as W
+    out = {}
+    for n, b in ((1, 64), (2, 64), (3, 128), (5, 128)):
+        w = W.WORKLOADS[n]
+        g = w.group
+        inp = W.make_inputs(n)
+        T, d, hq, hk = w.n_tokens, w.head_dim, w.n_q_heads, w.n_kv_heads
+        shape = rrp.layer_shape(hq, hk, d, w.rope_theta)
+        conv = (lambda a: to_device_bf16(a, dev)) if w.dtype == "bf16" else \
+            (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev))
+        q0, k0 = conv(inp["q"]), conv(inp["k"])
+        pos0 = torch.from_numpy(inp["pos"]).to(dev)
+        sm = None if inp["slot_mapping"] is None else torch.from_numpy(inp["slot_mapping"]).to(dev)
+        n_slots = inp["n_slots"]
+        src = inp["calib"] if inp["calib"] is not None else inp
+        est = w.estimator
+        cq = None if est == "k_only" else conv(src["q"])
+        angles = torch.empty(w.n_pairs, dtype=torch.float32, device=dev)
+        rrp.calibrate_angles(shape, cq, conv(src["k"]), torch.from_numpy(src["pos"]).to(dev),
+                             moments=rrp.new_moments(d, dev), estimator=est, angles_out=angles)
+        nbytes = w.bytes_per_token(group=g) * T
+        # one set: inputs, Q output and (for the prefill shapes) the cache slots it writes
+        set_bytes = 2 * q0.numel() * q0.element_size() + k0.numel() * k0.element_size() + 4 * T + \
+            (T * hk * (d // 2 + 2 * (d // g)))
+        n_sets = int(min(256, max(4, -(-ROTATED_FOOTPRINT // set_bytes))))
+        sets = []
+        shared_cache = None
+        if sm is not None:  # the decode batch scatters into one 256 x 32768-slot cache, shared by every set
+            shared_cache = rrp.new_kv4_cache(n_slots, hk, d, g, dev)
+        for _ in range(n_sets):
+            codes, scales = shared_cache if shared_cache is not None else rrp.new_kv4_cache(n_slots, hk, d, g, dev)
+            sets.append((q0.clone(), k0.clone(), pos0.clone(), torch.empty_like(q0), codes, scales))
+
+        def launcher(st):
+            q, k, pos, q_out, codes, scales = st
+            return lambda: rrp.rotate_quantize_qk(shape, q, k, pos, support_b=b, group=g, k_codes=codes,
+                                                  k_scales=scales, angles=angles, q_out=q_out, slot_mapping=sm,
+                                                  n_slots=n_slots)
+        us = graph_us_per_launch([launcher(st) for st in sets], stream)
+        footprint = n_sets * set_bytes
+        rec = {"workload": w.name, "n_tokens": T, "heads": f"{hq}/{hk}", "head_dim": d, "dtype": w.dtype,
+               "support_b": b, "group": g, "us_per_launch": us, "tokens_per_s": T / (us * 1e-6),
+               "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / (us * 1e-6) / 1e9,
+               "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+               "rotated_sets": n_sets, "footprint_bytes": footprint,
+               "cache_resident": footprint < INFINITY_CACHE_BYTES,
+               "timing": "HIP graph of one launch per set, replayed back to back"}
+        del sets
+        if with_oracle:
+            import oracle as O
+            shp = O.shape(hq, hk, d, w.rope_theta)
+            ang = angles.cpu().numpy()
+            t0 = time.perf_counter()
+            O.rotate_quantize_qk(shp, inp["q"], inp["k"], inp["pos"], ang, b, g,
+                                 slot_mapping=inp["slot_mapping"], n_slots=n_slots if sm is not None else None)
+            dt = time.perf_counter() - t0
+            rec["oracle"] = {"tokens_per_s": T / dt, "s": dt, "cores": O.max_threads(), "sample": "every token"}
+        out[f"C{n}"] = rec
+        torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -386,7 +535,11 @@ def main():
     copy_ms = ev[6].elapsed_time(ev[7]) / 10
     copy_ref = {"kernel": "torch device-to-device copy of Q (bf16)", "bytes_read_plus_written": copy_bytes,
                 "ms": copy_ms, "GBs": copy_bytes / (copy_ms * 1e-3) / 1e9}
+    ceiling = stream_ceiling(q, q_out, stream)
+    ceiling["rotate_frac_of_copy"] = achieved / ceiling["copy_GBs"]
+    per_config = None
     if not args.hot_path_only:
+        per_config = per_config_timing(dev, stream, not args.no_cpu_baseline)
         supporting.update(decode_latency_us(dev, stream))
         supporting.update(qkv_timing(w, shape, q, k, pos, angles, q_out, codes, scales, dev, stream, b, g))
         supporting.update(per_head_timing(w, q, k, pos, q_out, codes, scales, dev, stream, b, g))
@@ -419,6 +572,8 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": bytes_per_launch},
         "copy_reference": copy_ref,
+        "stream_ceiling": ceiling,
+        "per_config": per_config,
         "supporting": supporting,
         "wall_s_timed": t_wall,
     }

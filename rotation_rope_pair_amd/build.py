@@ -3,6 +3,8 @@
 Each .hip translation unit is compiled to an object in parallel, then linked
 into one shared library whose only exported symbols are the rrp_* entry points
 of include/rrp.h.  Packed-fp32 instructions are disabled for the device code.
+The benchmark's streaming-ceiling kernels (stream_probe.hip) go into a library
+of their own, libstream_probe.so, which only bench.py loads.
 """
 import concurrent.futures
 import os
@@ -17,6 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librrp.so")
 SOURCES = ["rrp_rotate.hip", "rrp_rotate_split.hip", "rrp_stats.hip", "rrp_decode.hip", "rrp_calib.hip",
            "rrp_abi.hip"]
+PROBE_LIB = os.path.join(HERE, "libstream_probe.so")
+PROBE_SOURCES = ["stream_probe.hip"]
 ARCH = os.environ.get("RRP_OFFLOAD_ARCH", "gfx950")
 
 
@@ -52,15 +56,21 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", LIB + ".tmp"]
+def _link(objs, lib, verbose):
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(lib + ".tmp", lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(7, os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

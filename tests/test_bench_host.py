@@ -60,3 +60,36 @@ def test_bytes_per_token_counts_every_stream(n):
     base = w.bytes_per_token(with_slot=False)
     assert w.bytes_per_token(with_slot=True) == base + 8
     assert w.bytes_per_token(with_slot=False, with_v=True) == base + hk * d * e + hk * d // 2 + 2 * hk * (d // g)
+
+
+def test_stream_probe_library_exports_and_rejects_bad_arguments():
+    """The streaming-ceiling kernels' library loads and checks sizes and alignment
+    on the host (nothing is launched on these calls)."""
+    import ctypes
+    if not os.path.exists(bench.PROBE_LIB):
+        from rotation_rope_pair_amd import build
+        build.build()
+    L = ctypes.CDLL(bench.PROBE_LIB)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.stream_probe_copy.argtypes = [vp, vp, sz, vp]
+    L.stream_probe_read.argtypes = [vp, sz, vp, vp]
+    L.stream_probe_write.argtypes = [vp, sz, vp]
+    p16, p8 = vp(1 << 20), vp((1 << 20) + 8)
+    assert L.stream_probe_copy(None, p16, 64, None) == 1 and L.stream_probe_copy(p16, p8, 64, None) == 1
+    assert L.stream_probe_copy(p16, p16, 40, None) == 1
+    assert L.stream_probe_read(p16, 64, None, None) == 1 and L.stream_probe_read(p8, 64, p16, None) == 1
+    assert L.stream_probe_write(p8, 64, None) == 1 and L.stream_probe_write(p16, 24, None) == 1
+
+
+def test_per_config_rotated_sets_span_past_the_infinity_cache():
+    """The per-workload timings rotate enough buffer sets to span 1 GiB (at least
+    four, at most 256), so launches stream from HBM except where 256 sets of a tiny
+    workload still fit the 256 MB cache, which the record then says."""
+    assert bench.ROTATED_FOOTPRINT >= 4 * bench.INFINITY_CACHE_BYTES
+    for n in (1, 2, 3, 5):
+        w = W.WORKLOADS[n]
+        T, d, hq, hk, g, e = w.n_tokens, w.head_dim, w.n_q_heads, w.n_kv_heads, w.group, w.elem_bytes
+        set_bytes = 2 * T * hq * d * e + T * hk * d * e + 4 * T + T * hk * (d // 2 + 2 * (d // g))
+        n_sets = int(min(256, max(4, -(-bench.ROTATED_FOOTPRINT // set_bytes))))
+        assert n_sets >= 4
+        assert n_sets * set_bytes >= bench.ROTATED_FOOTPRINT or n_sets == 256

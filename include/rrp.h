@@ -237,7 +237,7 @@ int rrp_quant_error_stats(const rrp_shape* shape, int32_t dtype, const void* k, 
                           double* stats_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes (host *bytes) of one rrp_quant_error_stats call: at most
- * 4096 * 5 * 8.  Errors as rrp_calibrate_angles_workspace_size. */
+ * 8192 * 5 * 8.  Errors as rrp_calibrate_angles_workspace_size. */
 int rrp_quant_error_stats_workspace_size(const rrp_shape* shape, int64_t n_tokens, size_t* bytes);
 
 /* rrp_quant_error_sweep -- the support interpolation in one call ("contributions"
@@ -248,9 +248,12 @@ int rrp_quant_error_stats_workspace_size(const rrp_shape* shape, int64_t n_token
  *   stats_out  double[log2(head_dim) + 1][8], row j = { E, N, sum of group max|y|,
  *              max of group max|y|, sum of group (max y - min y), n_groups,
  *              n_rows, b }  (overwritten).
- * Each row matches a separate rrp_quant_error_stats call up to the order of
- * fp64 rounding (the transform of support 2^j is built from the one of support
- * 2^(j-1) by one more butterfly stage).
+ * K is read once (one launch).  Each row matches a separate
+ * rrp_quant_error_stats call up to the order of fp64 rounding: the transform
+ * of support 2^j is built from the one of support 2^(j-1) by one more
+ * butterfly stage, kept without its 1 / sqrt(b) (applied to each group's
+ * scale constants and to the sums instead), and N is taken once, from the
+ * rotated row (every support's transform is orthogonal).
  * workspace     device, workspace_bytes >= rrp_quant_error_sweep_workspace_size
  *               (shape, n_tokens); may be NULL when that size is 0.
  * Errors as rrp_quant_error_stats. */

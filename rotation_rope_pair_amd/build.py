@@ -17,8 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librrp.so")
-SOURCES = ["rrp_rotate.hip", "rrp_rotate_split.hip", "rrp_stats.hip", "rrp_decode.hip", "rrp_calib.hip",
-           "rrp_abi.hip"]
+SOURCES = ["rrp_rotate.hip", "rrp_rotate_split.hip", "rrp_stats.hip", "rrp_sweep_bf16.hip", "rrp_sweep_f32.hip",
+           "rrp_decode.hip", "rrp_calib.hip", "rrp_abi.hip"]
 PROBE_LIB = os.path.join(HERE, "libstream_probe.so")
 PROBE_SOURCES = ["stream_probe.hip"]
 ARCH = os.environ.get("RRP_OFFLOAD_ARCH", "gfx950")
@@ -40,9 +40,15 @@ def common_flags():
     ]
 
 
+# Per-source flags.  The diagnostics kernels compare fp64 values with max / min
+# (group absmax and range); K rows are finite by contract, and without NaN
+# semantics those need no operand canonicalisation.
+EXTRA_FLAGS = {s: ["-fno-honor-nans"] for s in ("rrp_stats.hip", "rrp_sweep_bf16.hip", "rrp_sweep_f32.hip")}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -75,7 +75,7 @@ int stats_supports(const rrp_shape* s, bool sweep) {
 // Workspace bytes of one diagnostics call: the block partials [supports * 5][blocks].
 size_t stats_workspace_bytes(const rrp_shape* s, int64_t n_tokens, bool sweep) {
     if (n_tokens <= 0) return 0;
-    return (size_t)rrp::stats_blocks(n_tokens) * (size_t)stats_supports(s, sweep) * 5 * sizeof(double);
+    return (size_t)rrp::stats_blocks(n_tokens, sweep) * (size_t)stats_supports(s, sweep) * 5 * sizeof(double);
 }
 
 // A workspace of `have` bytes at `p` for a call needing `need` bytes.
@@ -351,7 +351,7 @@ int quant_error(const rrp_shape* shape, int32_t dtype, const void* k, const int3
     f.n_rows = (double)n_tokens * shape->n_kv_heads;
     f.n_groups = f.n_rows * (shape->head_dim / group);
     if (n_tokens > 0) {
-        const int nb = rrp::stats_blocks(n_tokens);
+        const int nb = rrp::stats_blocks(n_tokens, sweep);
         rrp::StatsArgs a{};
         a.k = k;
         a.pos = pos;

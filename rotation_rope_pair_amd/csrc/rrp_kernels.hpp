@@ -9,7 +9,7 @@
 namespace rrp {
 
 constexpr int kMaxCalibBlocks = 4096;  // block partials of the calibration pass
-constexpr int kMaxStatsBlocks = 4096;  // block partials of the diagnostic pass
+constexpr int kMaxStatsBlocks = 8192;  // block partials of the diagnostic pass
 
 struct CalibArgs {
     const void* q;
@@ -48,6 +48,9 @@ struct StatsArgs {
     int32_t support_b;
     int32_t group;
     int32_t angle_sets;  // 1: shared angle set; n_kv_heads: one per key head
+    int32_t bin;         // single support: channels of a group held by one lane (set by the launcher)
+    int32_t xmask;       // single support: lane position bits shared by a group (set by the launcher)
+    double wgt;          // single support: 1 / lanes sharing a group (set by the launcher)
     double rsqrt_b;
     float inv_freq[kMaxPairs];
 };
@@ -85,7 +88,7 @@ int calib_blocks(int64_t n_tokens, bool with_q, int hq, int hk, int head_dim, in
 hipError_t launch_calibrate(const CalibArgs& a, int dtype, int head_dim, int layout, hipStream_t st);
 hipError_t launch_calibrate_final(const CalibFinalArgs& a, hipStream_t st);
 
-int stats_blocks(int64_t n_tokens);
+int stats_blocks(int64_t n_tokens, bool sweep);
 hipError_t launch_stats(const StatsArgs& a, int n_blocks, int dtype, int head_dim, int layout, bool sweep,
                         hipStream_t st);
 hipError_t launch_stats_final(const StatsFinalArgs& a, hipStream_t st);

@@ -199,7 +199,7 @@ def test_stats_validation(lib):
     assert stt(out=None) == 1 and stt(k=None) == 1 and stt(b=5) == 1 and stt(g=3) == 1
     assert stt(out=ctypes.c_void_p((1 << 20) + 4)) == 2
     rc, need = ws_size(lib, "rrp_quant_error_stats", _shape(), 131072)
-    assert rc == 0 and 0 < need <= 4096 * 5 * 8
+    assert rc == 0 and 0 < need <= 8192 * 5 * 8
     assert ws_size(lib, "rrp_quant_error_stats", _shape(), 0) == (0, 0)
     assert stt(T=131072, ws=None) == 1 and stt(T=131072, ws_bytes=need - 1) == 1
     assert stt(T=131072, ws=ctypes.c_void_p((1 << 20) + 4)) == 2
@@ -214,9 +214,9 @@ def test_sweep_validation(lib):
     assert swp(shape=_shape(d=96)) == 3
     rc, need = ws_size(lib, "rrp_quant_error_sweep", _shape(), 131072)
     _, one = ws_size(lib, "rrp_quant_error_stats", _shape(), 131072)
-    assert rc == 0 and need == 8 * one                            # b = 1, 2, ..., 128: eight supports
+    assert rc == 0 and need == 8 * 4096 * 5 * 8                   # b = 1, 2, ..., 128: eight supports
     _, need64 = ws_size(lib, "rrp_quant_error_sweep", _shape(d=64), 131072)
-    assert need64 == 7 * one
+    assert need64 == 7 * 4096 * 5 * 8 and one == 8192 * 5 * 8
     assert swp(T=131072, ws_bytes=need - 8) == 1
 
 

@@ -414,6 +414,61 @@ def per_config_timing(dev, stream, with_oracle):
     return out
 
 
+def kernels_once(w, shape, q, k, pos, angles, q_out, codes, scales, dev, b, g, launches=2):
+    """Every kernel of the path and of its supporting passes, `launches` times
+    each, on the benchmark's inputs, and nothing else: a short run for
+    rocprofv3 counter passes (--pmc serialises every dispatch).  Prints the
+    kernels it ran as one JSON line (not the benchmark's line)."""
+    import numpy as np
+    import torch
+    import rotation_rope_pair_amd as rrp
+    from rotation_rope_pair_amd import workloads as W
+    hk, d = w.n_kv_heads, w.head_dim
+    v = to_device_bf16(W.make_v(w.number), dev)
+    vc, vs = rrp.new_kv4_cache(w.n_tokens, hk, d, g, dev)
+    moments = rrp.new_moments(d, dev)
+    shape_ph = rrp.layer_shape(w.n_q_heads, hk, d, w.rope_theta, angle_heads=hk)
+    moments_ph = rrp.new_moments(d, dev, n_sets=hk)
+    angles_ph = torch.empty((hk, d // 2), dtype=torch.float32, device=dev)
+    stats = torch.empty(8, dtype=torch.float64, device=dev)
+    sweep = torch.empty((len(rrp.sweep_supports(d)), 8), dtype=torch.float64, device=dev)
+    w5 = W.WORKLOADS[5]
+    bt = W.make_decode_batch(5)
+    shape5 = rrp.layer_shape(w5.n_q_heads, w5.n_kv_heads, w5.head_dim, w5.rope_theta)
+    q5 = to_device_bf16(bt["q"], dev)
+    codes5 = torch.from_numpy(bt["codes"]).to(dev)
+    scales5 = torch.from_numpy(bt["scales"].view(np.int16)).to(dev)
+    start5 = torch.from_numpy(bt["seq_start"]).to(dev)
+    lens5 = torch.from_numpy(bt["seq_len"]).to(dev)
+    scores5 = torch.empty((len(bt["seq_len"]), w5.n_q_heads, bt["max_len"]), dtype=torch.float32, device=dev)
+    runs = {
+        "rotate_quantize_qk": lambda: rrp.rotate_quantize_qk(
+            shape, q, k, pos, support_b=b, group=g, k_codes=codes, k_scales=scales, angles=angles, q_out=q_out),
+        "rotate_quantize_qkv": lambda: rrp.rotate_quantize_qkv(
+            shape, q, k, v, pos, support_b=b, group=g, k_codes=codes, k_scales=scales, v_codes=vc, v_scales=vs,
+            angles=angles, q_out=q_out),
+        "calibrate_angles": lambda: rrp.calibrate_angles(
+            shape, q, k, pos, moments=moments.zero_(), estimator="default", angles_out=angles),
+        "calibrate_angles_per_key_head": lambda: rrp.calibrate_angles(
+            shape_ph, q, k, pos, moments=moments_ph.zero_(), estimator="default", angles_out=angles_ph),
+        "rotate_quantize_qk_per_key_head": lambda: rrp.rotate_quantize_qk(
+            shape_ph, q, k, pos, support_b=b, group=g, k_codes=codes, k_scales=scales, angles=angles_ph,
+            q_out=q_out),
+        "quant_error_stats": lambda: rrp.quant_error_stats(
+            shape, k, pos, support_b=b, group=g, stats_out=stats, angles=angles),
+        "quant_error_sweep": lambda: rrp.quant_error_sweep(
+            shape, k, pos, group=g, stats_out=sweep, angles=angles),
+        "decode_scores": lambda: rrp.decode_scores(
+            shape5, q5, codes5, scales5, group=bt["group"], seq_start=start5, seq_len=lens5,
+            max_len=bt["max_len"], scores=scores5),
+    }
+    for name, fn in runs.items():
+        for _ in range(launches):
+            fn()
+        torch.cuda.synchronize()
+    print(json.dumps({"kernels_once": list(runs), "launches": launches}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +476,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hot-path-only", action="store_true")
+    ap.add_argument("--kernels-once", action="store_true",
+                    help="launch every kernel twice on the benchmark's inputs and exit (for counter passes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards over "
@@ -451,6 +508,9 @@ def main():
     moments = rrp.new_moments(d, dev)
     angles = torch.empty(d // 2, dtype=torch.float32, device=dev)
     rrp.calibrate_angles(shape, q, k, pos, moments=moments, estimator="default", angles_out=angles)
+    if args.kernels_once:
+        kernels_once(w, shape, q, k, pos, angles, q_out, codes, scales, dev, b, g)
+        return
     supporting = {}
     if not args.hot_path_only:
         reps = 10

@@ -128,29 +128,41 @@ void stats_kernel(const StatsArgs a) {
     block_stats_partials(acc, 0, red, a.partials);
 }
 
-// One wave per (set, statistic): lane l combines the partials of blocks l,
-// l + 64, ... in order, then a fixed xor butterfly folds the lanes (every lane
-// ends with the same value).  Partials are laid out [set * 5 + statistic][block];
-// stats_out row `set` is {E, N, sum absmax, max absmax, sum range, n_groups,
-// n_rows, support} (support 0 for a single-support call).
+// One block per (set, statistic): thread i combines the partials of blocks i,
+// i + 256, ... in order, a fixed xor butterfly folds each wave, and thread 0
+// combines the four waves in order.  Partials are laid out
+// [set * 5 + statistic][block]; stats_out row `set` is {E, N, sum absmax,
+// max absmax, sum range, n_groups, n_rows, support} (support 0 for a
+// single-support call); block n_sets * 5 writes the last three columns.
 __global__ __launch_bounds__(256) void stats_final_kernel(const StatsFinalArgs a) {
-    const int w = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    const int lane = (int)__lane_id();
-    if (w < a.n_sets * kNStat) {
-        const int set = w / kNStat, e = w % kNStat;
-        const double* part = a.partials + (size_t)w * a.n_blocks;
-        double v = 0.0;
-        for (int b = lane; b < a.n_blocks; b += 64) v = (e == 3) ? fmax(v, part[b]) : v + part[b];
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const double o = shfl_xor_d(v, m);
-            v = (e == 3) ? fmax(v, o) : v + o;
+    __shared__ double wsum[4];
+    const int w = (int)blockIdx.x;
+    const int tid = (int)threadIdx.x, lane = (int)__lane_id(), wave = tid >> 6;
+    if (w == a.n_sets * kNStat) {
+        if (tid < a.n_sets) {
+            a.stats_out[tid * 8 + 5] = a.n_groups;
+            a.stats_out[tid * 8 + 6] = a.n_rows;
+            a.stats_out[tid * 8 + 7] = a.sweep ? (double)(1 << tid) : 0.0;
         }
-        if (lane == 0) a.stats_out[set * 8 + e] = v;
-    } else if (w == a.n_sets * kNStat && lane < a.n_sets) {
-        a.stats_out[lane * 8 + 5] = a.n_groups;
-        a.stats_out[lane * 8 + 6] = a.n_rows;
-        a.stats_out[lane * 8 + 7] = a.sweep ? (double)(1 << lane) : 0.0;
+        return;
+    }
+    const int set = w / kNStat, e = w % kNStat;
+    const bool is_max = e == 3;
+    const double* part = a.partials + (size_t)w * a.n_blocks;
+    double v = 0.0;
+#pragma unroll 4
+    for (int b = tid; b < a.n_blocks; b += 256) v = is_max ? fmax(v, part[b]) : v + part[b];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const double o = shfl_xor_d(v, m);
+        v = is_max ? fmax(v, o) : v + o;
+    }
+    if (lane == 0) wsum[wave] = v;
+    __syncthreads();
+    if (tid == 0) {
+        double r = wsum[0];
+        for (int k = 1; k < 4; ++k) r = is_max ? fmax(r, wsum[k]) : r + wsum[k];
+        a.stats_out[set * 8 + e] = r;
     }
 }
 
@@ -229,8 +241,7 @@ hipError_t launch_stats(const StatsArgs& a, int n_blocks, int dtype, int head_di
 }
 
 hipError_t launch_stats_final(const StatsFinalArgs& a, hipStream_t st) {
-    const int waves = a.n_sets * kNStat + 1;
-    hipLaunchKernelGGL(stats_final_kernel, dim3((waves + 3) / 4), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(stats_final_kernel, dim3(a.n_sets * kNStat + 1), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

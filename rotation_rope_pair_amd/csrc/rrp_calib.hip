@@ -50,6 +50,13 @@ template <> struct Quad<float> {
     __device__ static T zero() { return T{0u, 0u, 0u, 0u}; }
 };
 
+// LDS slot of pair k in a token's RoPE table.  A lane reads the four pairs
+// 4s .. 4s + 3, so without padding the lanes of an 8-lane (16-lane) access fall
+// on 2 (4) distinct 16-byte slot groups; one pad slot after every four pairs
+// puts pair 4s + q at 5s + q, distinct modulo 16 for s < 16 (5 is odd).
+__device__ __forceinline__ int cslot(int k) { return k + (k >> 2); }
+template <int P> constexpr int ctab_slots() { return P + P / 4; }
+
 // MAXP: row passes loaded per step (a step is double-buffered across tokens).
 template <typename E, int D, int LAYOUT, int MAXP>
 __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
@@ -59,7 +66,7 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr size_t ROWB = (size_t)D * EB;
     using QT = typename Quad<E>::T;
-    __shared__ double2 tab_all[4][P];
+    __shared__ double2 tab_all[4][ctab_slots<P>()];
     __shared__ double red[4][P * kNSum];
 
     const int lane = (int)__lane_id();
@@ -134,12 +141,12 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
             if (lane < P) {
                 double sa, ca;
                 sincos_f64_of_f32(rope_angle_f32(p, invf), sa, ca);
-                tab[lane] = make_double2(ca, sa);
+                tab[cslot(lane)] = make_double2(ca, sa);
             }
             wave_lds_sync();
 #pragma unroll
             for (int j = 0; j < kCP; ++j) {
-                const double2 v = tab[s * kCP + j];
+                const double2 v = tab[cslot(s * kCP + j)];
                 c[j] = v.x;
                 sn[j] = v.y;
             }
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
 // set * (nbq + nbk) + (block's place in the set-group run), the layout
 // calib_reduce_kernel reads.
 constexpr int kSetWaves = 4;
-constexpr int kMaxSetGroup = 32;  // tokens per group, at most (32 KB of tables at d = 128)
+constexpr int kMaxSetGroup = 32;  // tokens per group, at most (40 KB of tables at d = 128)
 constexpr int kSetPasses = 8;     // row passes per wave and group, at least
 
 // Tokens per group of the per-set kernel for a stream with `heads` heads per set
@@ -237,7 +244,7 @@ void calib_sets_kernel(const CalibArgs a) {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr size_t ROWB = (size_t)D * EB;
     using QT = typename Quad<E>::T;
-    __shared__ double2 tab[kMaxSetGroup][P];
+    __shared__ double2 tab[kMaxSetGroup][ctab_slots<P>()];
 
     const int lane = (int)__lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -273,26 +280,37 @@ void calib_sets_kernel(const CalibArgs a) {
 #pragma unroll
         for (int m = 0; m < kNSum; ++m) acc[j][m] = 0.0;
 
-    // Token groups bs, bs + nb, ...: tokens tg * group + j.
+    // Token groups bs, bs + nb, ...: tokens tg * group + j.  A group's rows are
+    // r = j * g + h (token j of the group, head h0 + h of the set) and the lane
+    // takes r = pass * RP + grp; (j, h) is walked pass by pass with no division
+    // (RP = qrp * g + rrp), and each loaded pass carries its j (-1: no row).
     const int64_t n_groups = (a.n_tokens + tg - 1) / tg;
-    auto row_valid = [&](int64_t grp_t, int r, int64_t& t, int& h) {
-        const int j = r / g;
-        t = grp_t * tg + j;
-        h = h0 + (r - j * g);
-        return active && r < nrows && t < a.n_tokens;
-    };
-    auto load_step = [&](int64_t grp_t, int st, QT (&raw)[MAXP][2]) {
+    const int qrp = RP / g, rrp = RP % g;
+    const int j_first = grp / g, h_first = grp % g;
+    int lj = j_first, lh = h_first;  // the next pass to load
+    auto load_step = [&](int64_t grp_t, int st, QT (&raw)[MAXP][2], int (&rj)[MAXP]) {
+        if (st == 0) {
+            lj = j_first;
+            lh = h_first;
+        }
+        const unsigned char* gbase = src + ((size_t)grp_t * tg * nh_all + h0) * ROWB;
+        const int64_t tleft = a.n_tokens - grp_t * tg;  // tokens of the group that exist
 #pragma unroll
         for (int i = 0; i < MAXP; ++i) {
-            const int pass = st * MAXP + i;
-            int64_t t;
-            int h;
-            if (pass < npass && row_valid(grp_t, pass * RP + grp, t, h)) {
-                const unsigned char* rp = src + ((size_t)t * nh_all + h) * ROWB;
+            const bool ok = active && lj < tg && lj < tleft;
+            rj[i] = ok ? lj : -1;
+            if (ok) {
+                const unsigned char* rp = gbase + (size_t)(lj * nh_all + lh) * ROWB;
                 raw[i][0] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(rp + off0 * EB));
                 raw[i][1] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(rp + off1 * EB));
             } else {
                 raw[i][0] = raw[i][1] = Quad<E>::zero();
+            }
+            lh += rrp;
+            lj += qrp;
+            if (lh >= g) {
+                lh -= g;
+                ++lj;
             }
         }
     };
@@ -300,7 +318,10 @@ void calib_sets_kernel(const CalibArgs a) {
     int64_t gt = bs;
     int st = 0;
     QT cur[MAXP][2], nxt[MAXP][2];
-    if (gt < n_groups) load_step(gt, 0, cur);
+    int cj[MAXP], nj[MAXP];
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) cj[i] = nj[i] = -1;
+    if (gt < n_groups) load_step(gt, 0, cur, cj);
     // Retire the first step here: inside the loop `cur` is then always a copy
     // made after its wait, and the loop's first use of it needs no wait (which
     // would otherwise also take the next step's prefetch on every iteration).
@@ -313,7 +334,7 @@ void calib_sets_kernel(const CalibArgs a) {
             gn = gt + nb;
             sn_step = 0;
         }
-        if (gn < n_groups) load_step(gn, sn_step, nxt);
+        if (gn < n_groups) load_step(gn, sn_step, nxt, nj);
         if (st == 0) {
             __syncthreads();  // the previous group's table reads are complete
             for (int jj = wave; jj < tg; jj += kSetWaves) {
@@ -321,24 +342,21 @@ void calib_sets_kernel(const CalibArgs a) {
                 if (lane < P && t < a.n_tokens) {
                     double sa, ca;
                     sincos_f64_of_f32(rope_angle_f32(token_pos(a.pos, t), invf), sa, ca);
-                    tab[jj][lane] = make_double2(ca, sa);
+                    tab[jj][cslot(lane)] = make_double2(ca, sa);
                 }
             }
             __syncthreads();
         }
 #pragma unroll
         for (int i = 0; i < MAXP; ++i) {
-            const int pass = st * MAXP + i;
-            int64_t t;
-            int h;
-            if (!(pass < npass && row_valid(gt, pass * RP + grp, t, h))) continue;
-            const int j = (pass * RP + grp) / g;  // token of the row inside the group
+            const int j = cj[i];  // token of the row inside the group
+            if (j < 0) continue;
             float x0[4], x1[4];
             Quad<E>::unpack(cur[i][0], x0);
             Quad<E>::unpack(cur[i][1], x1);
 #pragma unroll
             for (int q = 0; q < kCP; ++q) {
-                const double2 cs = tab[j][s * kCP + q];
+                const double2 cs = tab[j][cslot(s * kCP + q)];
                 double xa, xb;
                 if constexpr (LAYOUT == 0) {
                     xa = x0[q];
@@ -363,6 +381,7 @@ void calib_sets_kernel(const CalibArgs a) {
         for (int i = 0; i < MAXP; ++i) {
             cur[i][0] = nxt[i][0];
             cur[i][1] = nxt[i][1];
+            cj[i] = nj[i];
         }
         gt = gn;
         st = sn_step;

@@ -97,8 +97,9 @@ def to_device_bf16(a, dev):
 
 def decode_latency_us(dev, stream, reps=200):
     """Per-launch time of the 256-token Mistral-shaped decode batch (slot scatter
-    into a 256 x 32768-slot KV4 cache), two ways: launches through the Python
-    binding (its argument checks cost more host time than the kernel takes), and
+    into a 256 x 32768-slot KV4 cache), three ways: launches through the Python
+    binding (its argument checks cost more host time than the kernel takes), the
+    binding's prepared call (checked and marshalled once, then re-issued), and
     back-to-back calls of the C entry point with the arguments marshalled once,
     which keeps the GPU busy and so times the kernel itself."""
     import torch
@@ -124,9 +125,13 @@ def decode_latency_us(dev, stream, reps=200):
 
     def launch_c():
         _abi.check("rrp_rotate_quantize_qk", L.rrp_rotate_quantize_qk(*args))
+    prepared = rrp.prepare_rotate_quantize_qk(shape5, q5, k5, pos5, support_b=128, group=w5.group, k_codes=c5,
+                                              k_scales=s5, angles=a5, q_out=q5o, slot_mapping=sm5,
+                                              n_slots=inp5["n_slots"])
     out = {}
     for key, fn in (("decode256_rotate_quantize_us", launch_c),
-                    ("decode256_rotate_quantize_us_python_binding", launch)):
+                    ("decode256_rotate_quantize_us_python_binding", launch),
+                    ("decode256_rotate_quantize_us_prepared_call", prepared)):
         for _ in range(10):
             fn()
         torch.cuda.synchronize()

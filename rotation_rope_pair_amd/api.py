@@ -276,13 +276,7 @@ def quant_error_sweep(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, gr
     _abi.check("rrp_quant_error_sweep", L.rrp_quant_error_sweep(*args))
 
 
-def decode_scores(shape: RrpShape, q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, *, group: int,
-                  seq_start: torch.Tensor, seq_len: torch.Tensor, max_len: int, scores: torch.Tensor,
-                  n_slots: Optional[int] = None, stream=None) -> None:
-    """Enqueue rrp_decode_scores: decode logits of the rotated queries q
-    [n_seqs][Hq][d] against the KV4 cache into scores fp32 [n_seqs][Hq][max_len]
-    (see include/rrp.h)."""
-    L = _abi.load()
+def _decode_args(shape, q, k_codes, k_scales, group, seq_start, seq_len, max_len, scores, n_slots, stream):
     d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
     B = int(seq_len.numel())
     dev = q.device
@@ -296,10 +290,66 @@ def decode_scores(shape: RrpShape, q: torch.Tensor, k_codes: torch.Tensor, k_sca
         _dev(seq_start, "seq_start", B, torch.int64, dev), _dev(seq_len, "seq_len", B, torch.int32, dev),
         int(max_len), _dev(scores, "scores", B * hq * int(max_len), torch.float32, dev), _stream_ptr(stream, dev),
     ]
+    return args
+
+
+def decode_scores(shape: RrpShape, q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, *, group: int,
+                  seq_start: torch.Tensor, seq_len: torch.Tensor, max_len: int, scores: torch.Tensor,
+                  n_slots: Optional[int] = None, stream=None) -> None:
+    """Enqueue rrp_decode_scores: decode logits of the rotated queries q
+    [n_seqs][Hq][d] against the KV4 cache into scores fp32 [n_seqs][Hq][max_len]
+    (see include/rrp.h)."""
+    L = _abi.load()
+    args = _decode_args(shape, q, k_codes, k_scales, group, seq_start, seq_len, max_len, scores, n_slots, stream)
     _abi.check("rrp_decode_scores", L.rrp_decode_scores(*args))
 
 
-__all__ = ["layer_shape", "angle_sets", "calibrate_angles_noalloc", "calibrate_workspace_bytes", "quant_error_stats_workspace_bytes",
+class PreparedCall:
+    """One C-ABI call whose tensors were checked and whose arguments were
+    marshalled once (by a prepare_* function): calling it enqueues the same
+    launch again, on the same tensors and stream, with no per-call Python
+    checks.  For loops that reuse fixed buffers (a decode step's queries,
+    positions, slot mapping and cache), whose contents may change between
+    calls.  The object holds references to the tensors and the shape, so their
+    storage stays alive; a tensor that is resized or replaced needs a new
+    prepared call.  The C entry point still validates its scalar arguments."""
+    __slots__ = ("_name", "_fn", "_args", "_keep")
+
+    def __init__(self, name, fn, args, keep):
+        self._name, self._fn, self._args, self._keep = name, fn, tuple(args), keep
+
+    def __call__(self) -> None:
+        status = self._fn(*self._args)
+        if status != _abi.RRP_OK:
+            _abi.check(self._name, status)
+
+
+def prepare_rotate_quantize_qk(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor, pos: torch.Tensor, *,
+                               support_b: int, group: int, k_codes: torch.Tensor, k_scales: torch.Tensor,
+                               angles: Optional[torch.Tensor] = None, q_out: Optional[torch.Tensor] = None,
+                               slot_mapping: Optional[torch.Tensor] = None, n_slots: Optional[int] = None,
+                               stream=None) -> PreparedCall:
+    """rotate_quantize_qk checked and marshalled once (see PreparedCall); the
+    stream is the one given, else the current stream at preparation."""
+    L = _abi.load()
+    args = _rotate_args(shape, q, k, None, pos, support_b, group, k_codes, k_scales, None, None, angles, q_out,
+                        slot_mapping, n_slots, None, None, None, None, None, stream)
+    keep = (shape, q, k, pos, angles, q_out, k_codes, k_scales, slot_mapping, stream)
+    return PreparedCall("rrp_rotate_quantize_qk", L.rrp_rotate_quantize_qk, args, keep)
+
+
+def prepare_decode_scores(shape: RrpShape, q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, *,
+                          group: int, seq_start: torch.Tensor, seq_len: torch.Tensor, max_len: int,
+                          scores: torch.Tensor, n_slots: Optional[int] = None, stream=None) -> PreparedCall:
+    """decode_scores checked and marshalled once (see PreparedCall)."""
+    L = _abi.load()
+    args = _decode_args(shape, q, k_codes, k_scales, group, seq_start, seq_len, max_len, scores, n_slots, stream)
+    keep = (shape, q, k_codes, k_scales, seq_start, seq_len, scores, stream)
+    return PreparedCall("rrp_decode_scores", L.rrp_decode_scores, args, keep)
+
+
+__all__ = ["layer_shape", "angle_sets", "calibrate_angles_noalloc", "calibrate_workspace_bytes",
+           "quant_error_stats_workspace_bytes", "PreparedCall", "prepare_rotate_quantize_qk", "prepare_decode_scores",
            "quant_error_sweep_workspace_bytes", "decode_scores", "quant_error_sweep", "sweep_supports",
            "rotate_quantize_qk", "rotate_quantize_qkv", "calibrate_angles", "quant_error_stats", "new_kv4_cache",
            "new_moments", "RrpError", "RrpShape", "ESTIMATORS", "RRP_F32", "RRP_BF16", "RRP_ROPE_HALF_SPLIT",

@@ -230,3 +230,16 @@ def test_binding_rejects_host_tensors_before_any_launch():
     scales = torch.zeros((4, 1, 1), dtype=torch.float16)
     with pytest.raises(ValueError, match="device"):
         rrp.rotate_quantize_qk(shape, None, k, pos, support_b=64, group=64, k_codes=codes, k_scales=scales)
+
+
+def test_prepared_call_checks_its_tensors_once_at_preparation():
+    """prepare_* runs the binding's tensor checks when it is called (host logic:
+    a host tensor is rejected before anything reaches the library)."""
+    torch = pytest.importorskip("torch")
+    import rotation_rope_pair_amd as rrp
+    shape = rrp.layer_shape(4, 1, 64, 10000.0)
+    x = torch.zeros(4 * 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        rrp.prepare_rotate_quantize_qk(shape, x, x, torch.zeros(1, dtype=torch.int32), support_b=64, group=64,
+                                       k_codes=torch.zeros((1, 1, 32), dtype=torch.uint8),
+                                       k_scales=torch.zeros(1, dtype=torch.float16))

@@ -514,7 +514,8 @@ def run_sweep(w, k, pos, angles, g, ah=0, layout=0):
 
 
 @pytest.mark.parametrize("n,g,with_angles", [(1, 64, True), (2, 64, True), (2, 64, False), (2, 4, True),
-                                              (3, 128, True), (3, 16, False)])
+                                              (2, 2, True), (3, 128, True), (3, 16, False), (3, 8, True),
+                                              (3, 2, False)])
 def test_quant_error_sweep_every_support_matches_oracle(n, g, with_angles):
     """One launch for every support b = 1 .. head_dim: each row equals the oracle's
     diagnostic at that b, and the single-support kernel's, to the stated tolerance."""
@@ -776,6 +777,63 @@ def grid_sample(T, n, seed):
     for r0 in range(0, T, GRID_STRIDE_TOKENS):
         edges += [r0, min(T, r0 + GRID_STRIDE_TOKENS) - 1]
     return np.unique(np.concatenate([sample_tokens(T, n, seed), np.array(edges)]))
+
+
+def degenerate_k(w, T, seed, regime):
+    """K rows of workload w's shape for one special case of the quantiser, so
+    the diagnostics' sums are dominated by it:
+    - "zero": all-zero rows and rows whose fp16 scale underflows to 0 (1e-9),
+      among ordinary rows;
+    - "saturated": +-1e6 rows and rows of ordinary values with a 1e6 outlier
+      channel, whose fp16 scale saturates at 65504 (codes clamp at +-7);
+    - "subnormal": rows of magnitude 10^U(-7, -6), whose fp16 scale is a coarse
+      subnormal; about a fifth of the groups have codes past +-7.5 before
+      clamping (the kernels' rare correction pass), some underflow to 0."""
+    rng = np.random.default_rng(seed)
+    hk, d = w.n_kv_heads, w.head_dim
+    k = rng.normal(0.0, 1.0, (T, hk, d))
+    if regime == "zero":
+        k[0::3] = 0.0
+        k[1::3] = 1e-9
+    elif regime == "saturated":
+        k[0::2] = 1e6 * np.sign(np.arange(d) - (d - 1) / 2.0) * rng.uniform(0.5, 2.0, (len(k[0::2]), hk, 1))
+        k[1::2, :, 5] = 1e6
+    else:
+        k *= 10.0 ** rng.uniform(-7.0, -6.0, (T, hk, 1))
+    k = k.astype(np.float32)
+    if w.dtype == "bf16":
+        return torch.from_numpy(k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return k
+
+
+@pytest.mark.parametrize("regime", ["zero", "saturated", "subnormal"])
+@pytest.mark.parametrize("n", [1, 3])
+def test_diagnostics_parity_degenerate_rows(n, regime):
+    """Stats at several (b, g) and the sweep at several g on K rows of one
+    special case of the quantiser (zero or underflowing scales, saturated
+    scales, coarse subnormal scales: the latter two go through the rare
+    clamped-code correction pass), against the oracle at the diagnostics
+    tolerances."""
+    w = W.WORKLOADS[n]
+    T = 40
+    inp = W.make_inputs(n, n_tokens=T)
+    k = degenerate_k(w, T, 3100 + n, regime)
+    pos = inp["pos"]
+    ang = random_angles(w.n_pairs, 3200 + n)
+    d = w.head_dim
+    for b in (1, 2, 16, d):
+        for g in (2, 16, d):
+            got = run_stats(w, k, pos, ang, b, g)
+            ref = O.quant_error_stats(oshape_of(w), k, pos, ang, b, g)
+            rel = np.abs(got[:5] - ref[:5]) / np.maximum(np.abs(ref[:5]), 1e-300)
+            assert np.all(rel <= STAT_TOL), (b, g, got, ref, rel)
+    supports = rrp.sweep_supports(d)
+    for g in (2, 8, d):
+        sw = run_sweep(w, k, pos, ang, g)
+        for j, b in enumerate(supports):
+            ref = O.quant_error_stats(oshape_of(w), k, pos, ang, b, g)
+            rel = np.abs(sw[j, :5] - ref[:5]) / np.maximum(np.abs(ref[:5]), 1e-300)
+            assert np.all(rel <= STAT_TOL), (g, b, sw[j], ref, rel)
 
 
 def long_inputs(n, T):

@@ -43,7 +43,9 @@ void stats_kernel(const StatsArgs a) {
     const double w = a.wgt;
     const int npass = (hk + R - 1) / R;
     const bool transpose = FULL || b > 8;          // butterflies on the run position
-    const bool back = transpose && a.group <= 8;   // groups inside a run: reduced in the natural layout
+    // groups smaller than half the head: reduced in the natural layout (fewer
+    // cross-lane stages than the transposed one, for the cost of transposing back)
+    const bool back = transpose && a.group < D / 2;
     const int64_t stride = (int64_t)gridDim.x * nwave;
 
     // rows past the last head read as zeros (they add nothing to any sum)
@@ -186,7 +188,7 @@ hipError_t launch_p(const StatsArgs& args, int n_blocks, hipStream_t st) {
     StatsArgs a = args;
     constexpr int L = SGeo<D>::L, K8 = SGeo<D>::K8, P = D / 2;
     const int g = a.group, b = a.support_b;
-    if (b > 8 && g > 8) {        // transposed layout: a group holds every run offset
+    if (b > 8 && g >= D / 2) {   // transposed layout: a group holds every run offset
         a.bin = g == D ? 16 : K8 * g / 8;
         a.xmask = L - 1;
     } else if (g <= 8) {         // natural layout: a run of the lane

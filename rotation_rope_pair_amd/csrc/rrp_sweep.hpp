@@ -19,8 +19,10 @@ namespace {
 // holds u = H_b x for b = 2^j, whose statistics are taken with the 1 / sqrt(b)
 // folded into each group's constants (group_stats, SCALED).  The in-run bits
 // act on the natural layout, the run-position bits after the LDS
-// transposition, and the half bit last.  The lane's sums are brought to the
-// normalised transform's (E / b, M, maxM and R / sqrt(b)) once, at the end.
+// transposition, and the half bit last (groups smaller than half the head
+// take their statistics back in the natural layout).  The lane's sums are
+// brought to the normalised transform's (E / b, M, maxM and R / sqrt(b)) once,
+// at the end.
 // ---------------------------------------------------------------------------
 template <int D> struct Log2;
 template <> struct Log2<64> { static constexpr int value = 6; };
@@ -119,6 +121,17 @@ void sweep_kernel(const StatsArgs a) {
         // the run-position bits (supports 16 .. D/2), transposed, then the half bit (support D)
         double tt[16];
         transpose_in<D>(tb, r, s, x, tt);
+        // Statistics of the support just reached.  Groups smaller than half the
+        // head are reduced in the natural layout (transposed back into x): there
+        // they need fewer cross-lane stages.
+        auto stats_t = [&](int j) {
+            if constexpr (G < D / 2) {
+                transpose_out<D>(tb, r, s, tt, x);
+                group_stats<GR::BINN, L, true, FIX>(xv, GR::XMN, GR::WN, acc[j], far, rsqrt_pow2(j), sqrt_pow2(j));
+            } else {
+                group_stats<GR::BINT, L, true, FIX>(tt, GR::XMT, GR::WT, acc[j], far, rsqrt_pow2(j), sqrt_pow2(j));
+            }
+        };
 #pragma unroll
         for (int h = 1, j = 4; h < L; h <<= 1, ++j) {
 #pragma unroll
@@ -133,7 +146,7 @@ void sweep_kernel(const StatsArgs a) {
                             tt[e0] = p + q;
                             tt[e1] = p - q;
                         }
-            group_stats<GR::BINT, L, true, FIX>(tt, GR::XMT, GR::WT, acc[j], far, rsqrt_pow2(j), sqrt_pow2(j));
+            stats_t(j);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -141,7 +154,7 @@ void sweep_kernel(const StatsArgs a) {
             tt[e] = p + q;
             tt[8 + e] = p - q;
         }
-        group_stats<GR::BINT, L, true, FIX>(tt, GR::XMT, GR::WT, acc[NJ - 1], far, rsqrt_pow2(NJ - 1), sqrt_pow2(NJ - 1));
+        stats_t(NJ - 1);
     };
     int64_t t = (int64_t)blockIdx.x * nwave + wave;
     int ps = 0;

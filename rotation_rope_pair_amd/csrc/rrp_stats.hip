@@ -17,10 +17,12 @@ void stats_kernel(const StatsArgs a) {
     constexpr int P = G::P, L = G::L, R = G::R;
     constexpr size_t ROWB = (size_t)D * ElemInfo<E>::bytes;
     constexpr int WAVES = kStatsWaves;
-    __shared__ double2 tab_all[WAVES][PH ? kSetStride * P : tab_entries<P>()];
-    __shared__ double2 phi_all[PH ? kSetStride * P : 1];
+    __shared__ double2 tab_all[WAVES][tab_entries<P>()];
+    // the passes' transpositions; with one angle set per key head it first
+    // stages the sets' (cos, sin)(phi) for the lanes to take into registers
     __shared__ double2 tbuf_all[WAVES][G::SLOTS];
     __shared__ double red[4][kNStat];
+    static_assert(!PH || WAVES * G::SLOTS >= kSetStride * P, "staging of the angle sets");
 
     const int lane = (int)__lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -31,13 +33,26 @@ void stats_kernel(const StatsArgs a) {
     double2* tb = tbuf_all[wave];
 
     double cphi = 1.0, sphi = 0.0;
-    if constexpr (PH) load_angle_sets<P>(phi_all, a.angles, a.angle_sets);
-    else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
-    const float invf = lane_inv_freq(a.inv_freq, lane, P);
     int kidx[8];
     pair_index_of_lane<D, LAYOUT, 8>(s, kidx);
+    // One angle set per key head (at most 8, so a token's key rows are one pass
+    // and the lane's row r is key head r, hence set r, for the whole kernel):
+    // the lane keeps (cos, sin)(phi) of its pairs in that set in registers and
+    // composes them with the token's bare RoPE table (rotate_sets).
+    double2 cs_phi[PH ? 8 : 1];
+    if constexpr (PH) {
+        double2* stage = &tbuf_all[0][0];
+        load_angle_sets<P>(stage, a.angles, a.angle_sets);  // ends with a block barrier
+        const int set = r < a.hk ? r : 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kidx[j] = PH ? kidx[j] * kSetStride : tab_index(kidx[j]);
+        for (int j = 0; j < 8; ++j) cs_phi[j] = stage[kidx[j] * kSetStride + set];
+        __syncthreads();  // read before the buffer serves the transpositions
+    } else if (a.angles != nullptr && lane < P) {
+        sincos_f64_of_f32(a.angles[lane], sphi, cphi);
+    }
+    const float invf = lane_inv_freq(a.inv_freq, lane, P);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kidx[j] = tab_index(kidx[j]);
     const unsigned char* kb = static_cast<const unsigned char*>(a.k);
     const int hk = a.hk, b = FULL ? D : a.support_b, xmask = a.xmask;
     const double w = a.wgt;
@@ -60,12 +75,12 @@ void stats_kernel(const StatsArgs a) {
     StatAcc acc;
     // One pass (R rows of a token): FIX false is the main pass, FIX true the
     // rare correction pass over the same rows.
-    auto pass = [&](auto fixc, const u32x4 (&raw)[IO::NR], int ps, bool& far) {
+    auto pass = [&](auto fixc, const u32x4 (&raw)[IO::NR], bool& far) {
         constexpr bool FIX = decltype(fixc)::value;
-        const int row = ps * R + r;
         double x[2][8];
         IO::unpack(raw, x);
-        rotate_lds<LAYOUT, FOLD>(x, PH ? tab + (row < hk ? row : 0) : tab, kidx);
+        if constexpr (PH) rotate_sets<LAYOUT, FOLD>(x, tab, kidx, cs_phi, a.rsqrt_b);
+        else rotate_tab<LAYOUT, FOLD>(x, tab, kidx);
         if (b > 1) fwht_inreg_stage<8, 1>(x);
         if (b > 2) fwht_inreg_stage<8, 2>(x);
         if (b > 4) fwht_inreg_stage<8, 4>(x);
@@ -111,16 +126,16 @@ void stats_kernel(const StatsArgs a) {
         }
         if (tn < a.n_tokens) load_pass(tn, pn, nxt);
         if (ps == 0) {
-            if constexpr (PH) token_tables_sets<D, FOLD>(nullptr, tab, lane, token_pos(a.pos, t), invf, phi_all, a.angle_sets, a.rsqrt_b);
+            if constexpr (PH) token_table64<D, false>(tab, lane, token_pos(a.pos, t), invf, 1.0, 0.0, 1.0);
             else token_table64<D, FOLD>(tab, lane, token_pos(a.pos, t), invf, cphi, sphi, a.rsqrt_b);
         }
         bool far = false;
-        pass(BoolC<false>{}, cur, ps, far);
+        pass(BoolC<false>{}, cur, far);
         pin(acc);
         if (__ballot(far) != 0) {  // rare: redo the pass, adding only the clamped codes' change
             u32x4 raw[IO::NR];
             load_pass(t, ps, raw);
-            pass(BoolC<true>{}, raw, ps, far);
+            pass(BoolC<true>{}, raw, far);
         }
 #pragma unroll
         for (int k = 0; k < IO::NR; ++k) cur[k] = nxt[k];

@@ -294,9 +294,22 @@ __device__ __forceinline__ void group_stats(const double (&t)[16], int xmask, do
     }
 }
 
+// One table entry: (C, S) = (cos, sin)(alpha + phi) / sqrt(b) composed by
+// products of the fp64 (cos, sin) of alpha (ca, sa) and of phi (cp, sp), or
+// (C + S, C - S) with the half butterfly folded in (FOLD).  Written with
+// explicit fused operations so that every caller gets the same doubles (the
+// shared-set table and the per-set composition below).
+template <bool FOLD>
+__device__ __forceinline__ double2 compose_entry(double ca, double sa, double cp, double sp, double rs) {
+    const double C = fma(ca, cp, -(sa * sp)) * rs;
+    const double S = fma(sa, cp, ca * sp) * rs;
+    return FOLD ? make_double2(C + S, C - S) : make_double2(C, S);
+}
+
 // The token's fp64 table of the shared angle set: entry of pair k at
-// tab_index(k), (C, S) = (cos, sin)(alpha_k + phi_k) / sqrt(b) composed by
-// products, or (C + S, C - S) with the half butterfly folded in (FOLD).
+// tab_index(k) (compose_entry of the pair's RoPE angle and phi_k).  With one
+// angle set per key head the table holds the bare RoPE (cos, sin) instead
+// (cphi = 1, sphi = 0, rs = 1, no fold), composed per row (rotate_sets).
 template <int D, bool FOLD>
 __device__ __forceinline__ void token_table64(double2* tab, int lane, int p, float invf, double cphi, double sphi,
                                               double rs) {
@@ -305,10 +318,86 @@ __device__ __forceinline__ void token_table64(double2* tab, int lane, int p, flo
     if (lane < P) {
         double sa, ca;
         sincos_f64_of_f32(rope_angle_f32(p, invf), sa, ca);
-        const double C = (ca * cphi - sa * sphi) * rs, S = (sa * cphi + ca * sphi) * rs;
-        tab[tab_index(lane)] = FOLD ? make_double2(C + S, C - S) : make_double2(C, S);
+        tab[tab_index(lane)] = compose_entry<FOLD>(ca, sa, cphi, sphi, rs);
     }
     wave_lds_sync();
+}
+
+// One pair (a, b) turned by a table entry e, with explicit fused operations
+// (so the shared-set and the per-set paths give the same doubles):
+// (a C - b S, b C + a S), or (a U + b V, a V - b U) with the half butterfly
+// folded in.
+template <bool FOLD>
+__device__ __forceinline__ void turn_pair(double& a, double& b, double2 e) {
+    const double a0 = a, b0 = b;
+    if constexpr (FOLD) {
+        a = fma(a0, e.x, b0 * e.y);
+        b = fma(a0, e.y, -(b0 * e.x));
+    } else {
+        a = fma(a0, e.x, -(b0 * e.y));
+        b = fma(b0, e.x, a0 * e.y);
+    }
+}
+
+// The two channels of pair slot j of a lane (see pair_index_of_lane).
+template <int LAYOUT>
+__device__ __forceinline__ void pair_slots(double (&x)[2][8], int j, double*& pa, double*& pb) {
+    if constexpr (LAYOUT == 0) {
+        pa = &x[0][j];
+        pb = &x[1][j];
+    } else {
+        pa = &x[j / 4][2 * (j % 4)];
+        pb = pa + 1;
+    }
+}
+
+// RoPE + R_phi of the lane's pairs from the token's composed table (shared
+// angle set): entry kidx[j] for pair slot j.
+template <int LAYOUT, bool FOLD>
+__device__ __forceinline__ void rotate_tab(double (&x)[2][8], const double2* tab, const int (&kidx)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        double* pa;
+        double* pb;
+        pair_slots<LAYOUT>(x, j, pa, pb);
+        turn_pair<FOLD>(*pa, *pb, tab[kidx[j]]);
+    }
+}
+
+// RoPE + R_phi of the lane's pairs with one angle set per key head: the bare
+// RoPE (cos, sin) of pair kidx[j] from the token's table, composed with the
+// row's set angles (cos, sin)(phi) held in registers (cs_phi[j]), exactly as
+// the shared-set table composes them.
+template <int LAYOUT, bool FOLD>
+__device__ __forceinline__ void rotate_sets(double (&x)[2][8], const double2* tab, const int (&kidx)[8],
+                                            const double2 (&cs_phi)[8], double rs) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const double2 ra = tab[kidx[j]];
+        double* pa;
+        double* pb;
+        pair_slots<LAYOUT>(x, j, pa, pb);
+        turn_pair<FOLD>(*pa, *pb, compose_entry<FOLD>(ra.x, ra.y, cs_phi[j].x, cs_phi[j].y, rs));
+    }
+}
+
+// The same with the row's set angles read from the block's table phi (entry
+// (k, set) at k * kSetStride + set): phirow = phi + (the lane's first pair) *
+// kSetStride + set, and pair slot j sits a compile-time offset further.
+template <int D, int LAYOUT, bool FOLD>
+__device__ __forceinline__ void rotate_sets_lds(double (&x)[2][8], const double2* tab, const int (&kidx)[8],
+                                                const double2* phirow, double rs) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        constexpr int Q = D / 4;
+        const int dk = LAYOUT == 0 ? j : (j / 4) * Q + (j % 4);  // pair of slot j minus the lane's first pair
+        const double2 ra = tab[kidx[j]];
+        const double2 ph = phirow[dk * kSetStride];
+        double* pa;
+        double* pb;
+        pair_slots<LAYOUT>(x, j, pa, pb);
+        turn_pair<FOLD>(*pa, *pb, compose_entry<FOLD>(ra.x, ra.y, ph.x, ph.y, rs));
+    }
 }
 
 template <bool B> struct BoolC {

@@ -66,7 +66,7 @@ void sweep_kernel(const StatsArgs a) {
     constexpr int NJ = Log2<D>::value + 1;  // supports 2^0 .. 2^(NJ-1)
     constexpr size_t ROWB = (size_t)D * ElemInfo<E>::bytes;
     constexpr int WAVES = kStatsWaves;
-    __shared__ double2 tab_all[WAVES][PH ? kSetStride * P : tab_entries<P>()];
+    __shared__ double2 tab_all[WAVES][tab_entries<P>()];
     __shared__ double2 phi_all[PH ? kSetStride * P : 1];
     __shared__ double2 tbuf_all[WAVES][Geo_::SLOTS];
     __shared__ double red[4][kNStat];
@@ -80,13 +80,23 @@ void sweep_kernel(const StatsArgs a) {
     double2* tb = tbuf_all[wave];
 
     double cphi = 1.0, sphi = 0.0;
-    if constexpr (PH) load_angle_sets<P>(phi_all, a.angles, a.angle_sets);
-    else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
-    const float invf = lane_inv_freq(a.inv_freq, lane, P);
     int kidx[8];
     pair_index_of_lane<D, LAYOUT, 8>(s, kidx);
+    // One angle set per key head: the lane's row is key head r (set r) for the
+    // whole kernel (see stats_kernel); each pass composes its pairs' entries of
+    // set r in the block's (cos, sin)(phi) table with the token's bare RoPE
+    // table (the sweep's registers leave no room to keep them, as the
+    // single-support kernel does).
+    const double2* phirow = phi_all;
+    if constexpr (PH) {
+        load_angle_sets<P>(phi_all, a.angles, a.angle_sets);  // ends with a block barrier
+        phirow = phi_all + kidx[0] * kSetStride + (r < a.hk ? r : 0);
+    } else if (a.angles != nullptr && lane < P) {
+        sincos_f64_of_f32(a.angles[lane], sphi, cphi);
+    }
+    const float invf = lane_inv_freq(a.inv_freq, lane, P);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kidx[j] = PH ? kidx[j] * kSetStride : tab_index(kidx[j]);
+    for (int j = 0; j < 8; ++j) kidx[j] = tab_index(kidx[j]);
     const unsigned char* kb = static_cast<const unsigned char*>(a.k);
     const int hk = a.hk;
     const int npass = (hk + R - 1) / R;
@@ -105,10 +115,10 @@ void sweep_kernel(const StatsArgs a) {
     // rare correction pass over the same rows.
     auto pass = [&](auto fixc, const u32x4 (&raw)[IO::NR], int ps, StatAcc (&acc)[NJ], bool& far) {
         constexpr bool FIX = decltype(fixc)::value;
-        const int row = ps * R + r;
         double x[2][8];
         IO::unpack(raw, x);
-        rotate_lds<LAYOUT, false>(x, PH ? tab + (row < hk ? row : 0) : tab, kidx);
+        if constexpr (PH) rotate_sets_lds<D, LAYOUT, false>(x, tab, kidx, phirow, 1.0);
+        else rotate_tab<LAYOUT, false>(x, tab, kidx);
         double(&xv)[16] = reinterpret_cast<double(&)[16]>(x);
         // support 1 (with the energy), then the in-run bits: supports 2, 4, 8
         group_stats<GR::BINN, L, false, FIX>(xv, GR::XMN, GR::WN, acc[0], far);
@@ -171,7 +181,7 @@ void sweep_kernel(const StatsArgs a) {
         }
         if (tn < a.n_tokens) load_pass(tn, pn, nxt);
         if (ps == 0) {
-            if constexpr (PH) token_tables_sets<D, false>(nullptr, tab, lane, token_pos(a.pos, t), invf, phi_all, a.angle_sets, 1.0);
+            if constexpr (PH) token_table64<D, false>(tab, lane, token_pos(a.pos, t), invf, 1.0, 0.0, 1.0);
             else token_table64<D, false>(tab, lane, token_pos(a.pos, t), invf, cphi, sphi, 1.0);
         }
         bool far = false;

@@ -635,9 +635,14 @@ def test_per_head_identical_sets_equal_the_shared_path():
             if x.dtype == torch.bfloat16:
                 x, y = x.view(torch.int16), y.view(torch.int16)
             assert torch.equal(x, y), (b, key)
-    st_a = run_stats(w, inp["k"], inp["pos"], shared, 128, 128)
-    st_c = run_stats(w, inp["k"], inp["pos"], sets, 128, 128, ah=w.n_kv_heads)
-    assert np.array_equal(st_a, st_c)
+    for b, g in ((128, 128), (16, 16), (2, 128), (64, 8)):
+        st_a = run_stats(w, inp["k"], inp["pos"], shared, b, g)
+        st_c = run_stats(w, inp["k"], inp["pos"], sets, b, g, ah=w.n_kv_heads)
+        assert np.array_equal(st_a, st_c), (b, g, st_a, st_c)
+    for g in (128, 16):
+        sw_a = run_sweep(w, inp["k"], inp["pos"], shared, g)
+        sw_c = run_sweep(w, inp["k"], inp["pos"], sets, g, ah=w.n_kv_heads)
+        assert np.array_equal(sw_a, sw_c), (g, sw_a, sw_c)
 
 
 @pytest.mark.parametrize("n,b,g", [(2, 64, 64), (3, 128, 128), (3, 2, 16)])

@@ -291,11 +291,16 @@ int rrp_quant_error_sweep_workspace_size(const rrp_shape* shape, int64_t n_token
  * group       the group size the cache was written with (power of two in [2, head_dim]).
  * seq_start   int64[n_seqs], 8-byte aligned: slot of key 0 of each sequence.
  * seq_len     int32[n_seqs]: keys per sequence (values above max_len are cut to max_len).
- * max_len     row length of `scores`.
+ * max_len     row length of `scores`, at most 2^31 - 513 (else RRP_ERR_UNSUPPORTED).
  * scores      fp32 [n_seqs][n_q_heads][max_len].  Only j < min(seq_len[b], max_len)
  *             is written; a key whose slot lies outside [0, n_slots) gets NaN.
  * n_slots     cache capacity in slots, >= 1.
- * n_seqs == 0 or max_len == 0 is a no-op returning RRP_OK. */
+ * n_seqs == 0 or max_len == 0 is a no-op returning RRP_OK.  Any number of
+ * sequences is accepted: a batch larger than one grid holds is enqueued as
+ * several launches over consecutive sequence ranges.  A sequence takes
+ * ceil(max_len / 256) * n_kv_heads waves; where the one-dimensional grid is
+ * used (n_kv_heads not a multiple of 4, or more than 65535 key chunks) and that
+ * exceeds the 67108860 waves one grid holds, RRP_ERR_UNSUPPORTED. */
 int rrp_decode_scores(const rrp_shape* shape, int32_t dtype, const void* q, int64_t n_seqs,
                       const uint8_t* k_codes, const uint16_t* k_scales, int32_t group, int64_t n_slots,
                       const int64_t* seq_start, const int32_t* seq_len, int32_t max_len, float* scores,

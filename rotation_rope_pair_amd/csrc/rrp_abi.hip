@@ -419,6 +419,8 @@ RRP_EXPORT int rrp_decode_scores(const rrp_shape* shape, int32_t dtype, const vo
     if (n_seqs < 0 || n_slots < 0 || max_len < 0) return RRP_ERR_INVALID_ARG;
     if (n_seqs == 0 || max_len == 0) return RRP_OK;
     if (n_slots == 0) return RRP_ERR_INVALID_ARG;  // an empty cache holds no key to read
+    // key indices are 32-bit: a chunk's end plus one tile stays below 2^31
+    if (max_len > INT32_MAX - 2 * rrp::decode_chunk_keys()) return RRP_ERR_UNSUPPORTED;
     if (q == nullptr || k_codes == nullptr || k_scales == nullptr || seq_start == nullptr || seq_len == nullptr ||
         scores == nullptr)
         return RRP_ERR_INVALID_ARG;
@@ -441,7 +443,7 @@ RRP_EXPORT int rrp_decode_scores(const rrp_shape* shape, int32_t dtype, const vo
     a.group_heads = hq / hk;
     a.max_len = max_len;
     a.vec_store = (max_len % 4 == 0 && aligned(scores, 16)) ? 1 : 0;
-    if ((n_seqs * a.n_chunks * hk + 3) / 4 > 0x7FFFFFFF) return RRP_ERR_INVALID_ARG;  // grid too large
+    if (rrp::decode_launches(n_seqs, a.n_chunks, hk) < 1) return RRP_ERR_UNSUPPORTED;  // one sequence overfills a grid
     const hipError_t e = rrp::launch_decode_scores(a, dtype, d, group, (hipStream_t)stream);
     return e == hipSuccess ? RRP_OK : RRP_ERR_HIP;
 }

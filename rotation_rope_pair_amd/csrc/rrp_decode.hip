@@ -149,13 +149,13 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
         // grid (hk / 4, chunks, sequences): the indices need no division
         kvh = (int)blockIdx.x * 4 + wave;
         chunk = (int)blockIdx.y;
-        b = blockIdx.z;
+        b = a.seq_base + blockIdx.z;
     } else {
         const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
         kvh = (int)(wid % hk);
         const int64_t rest = wid / hk;
         chunk = (int)(rest % a.n_chunks);
-        b = rest / a.n_chunks;
+        b = a.seq_base + rest / a.n_chunks;
     }
     if (b >= a.n_seqs) return;
     int len = a.seq_len[b];
@@ -523,23 +523,53 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
     else body(std::false_type{});
 }
 
-template <typename E, int D>
-hipError_t launch_d(const DecodeArgs& a0, int group, hipStream_t st) {
+// A dispatch covers at most 2^32 - 1 work-items per grid dimension, and the y
+// and z block counts at most 65535 each.
+constexpr int64_t kMaxGridThreads = 0xFFFFFFFFll;
+constexpr int64_t kMaxGridYZ = 65535;
+
+// Sequences one launch may take; 0 if a single sequence does not fit.
+int64_t decode_seqs_per_launch(int64_t n_chunks, int hk) {
+    const bool grid3d = hk % 4 == 0 && n_chunks <= kMaxGridYZ;
+    if (grid3d) return kMaxGridYZ;
+    const int64_t waves_per_seq = n_chunks * hk;
+    const int64_t max_waves = kMaxGridThreads / 256 * 4;
+    const int64_t s = max_waves / waves_per_seq;
+    return s < kMaxGridYZ ? s : kMaxGridYZ;
+}
+
+template <typename E, int D, int GS>
+hipError_t launch_range(DecodeArgs a, hipStream_t st) {
     // Four key heads of one (sequence, chunk) per block.  With hk a multiple of 4
-    // (and the chunk and sequence counts within the y and z grid limits) the
-    // block's place comes straight from a 3-D grid, else from a 1-D one.
-    DecodeArgs a = a0;
-    dim3 grid;
-    a.grid3d = (a.hk % 4 == 0 && a.n_chunks <= 65535 && a.n_seqs <= 65535) ? 1 : 0;
-    if (a.grid3d) {
-        grid = dim3((unsigned)(a.hk / 4), (unsigned)a.n_chunks, (unsigned)a.n_seqs);
-    } else {
-        const int64_t waves = a.n_seqs * a.n_chunks * a.hk;
-        grid = dim3((unsigned)((waves + 3) / 4));
+    // (and the chunk count within the y grid limit) the block's place comes
+    // straight from a 3-D grid, else from a 1-D one.  Batches with more sequences
+    // than one grid holds go out as consecutive launches over sequence ranges.
+    a.grid3d = (a.hk % 4 == 0 && a.n_chunks <= kMaxGridYZ) ? 1 : 0;
+    const int64_t per_launch = decode_seqs_per_launch(a.n_chunks, a.hk);
+    if (per_launch < 1) return hipErrorInvalidConfiguration;
+    const int64_t n_seqs = a.n_seqs;
+    for (int64_t s0 = 0; s0 < n_seqs; s0 += per_launch) {
+        const int64_t ns = n_seqs - s0 < per_launch ? n_seqs - s0 : per_launch;
+        a.seq_base = s0;
+        a.n_seqs = s0 + ns;  // the kernel's bound: the 1-D grid's last block may overhang the range
+        dim3 grid;
+        if (a.grid3d) {
+            grid = dim3((unsigned)(a.hk / 4), (unsigned)a.n_chunks, (unsigned)ns);
+        } else {
+            const int64_t waves = ns * a.n_chunks * a.hk;
+            grid = dim3((unsigned)((waves + 3) / 4));
+        }
+        hipLaunchKernelGGL((decode_scores_kernel<E, D, GS>), grid, dim3(256), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    const dim3 block(256);
+    return hipSuccess;
+}
+
+template <typename E, int D>
+hipError_t launch_d(const DecodeArgs& a, int group, hipStream_t st) {
 #define RRP_G(GS) \
-    if (group == GS) { hipLaunchKernelGGL((decode_scores_kernel<E, D, GS>), grid, block, 0, st, a); return hipGetLastError(); }
+    if (group == GS) return launch_range<E, D, GS>(a, st);
     RRP_G(2) RRP_G(4) RRP_G(8) RRP_G(16) RRP_G(32) RRP_G(64)
     if constexpr (D >= 128) { RRP_G(128) }
 #undef RRP_G
@@ -548,7 +578,11 @@ hipError_t launch_d(const DecodeArgs& a0, int group, hipStream_t st) {
 
 }  // namespace
 
-int64_t decode_chunks(int max_len) { return (max_len + kKeysPerWave - 1) / kKeysPerWave; }
+int64_t decode_chunks(int max_len) { return ((int64_t)max_len + kKeysPerWave - 1) / kKeysPerWave; }
+int64_t decode_launches(int64_t n_seqs, int64_t n_chunks, int hk) {
+    const int64_t per_launch = decode_seqs_per_launch(n_chunks, hk);
+    return per_launch < 1 ? 0 : (n_seqs + per_launch - 1) / per_launch;
+}
 int decode_chunk_keys() { return kKeysPerWave; }
 
 hipError_t launch_decode_scores(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t st) {

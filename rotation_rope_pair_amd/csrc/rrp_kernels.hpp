@@ -72,7 +72,7 @@ struct DecodeArgs {
     const int64_t* seq_start;  // [n_seqs] slot of key 0
     const int32_t* seq_len;    // [n_seqs] keys per sequence
     float* scores;             // [n_seqs][hq][max_len]
-    int64_t n_seqs;
+    int64_t n_seqs;            // sequences in the batch (in a launch: one past its last sequence)
     int64_t n_slots;
     int64_t n_chunks;          // key chunks per sequence (one wave each)
     int32_t hq;
@@ -80,7 +80,8 @@ struct DecodeArgs {
     int32_t group_heads;       // hq / hk query heads per key head
     int32_t max_len;
     int32_t vec_store;         // scores rows are 16-byte aligned: store 4 logits at once
-    int32_t grid3d;            // grid (hk / 4, n_chunks, n_seqs) instead of one dimension (set by the launcher)
+    int32_t grid3d;            // grid (hk / 4, n_chunks, sequences) instead of one dimension (set by the launcher)
+    int64_t seq_base;          // first sequence of this launch (the launcher splits long batches)
 };
 
 
@@ -94,6 +95,7 @@ hipError_t launch_stats(const StatsArgs& a, int n_blocks, int dtype, int head_di
 hipError_t launch_stats_final(const StatsFinalArgs& a, hipStream_t st);
 
 int64_t decode_chunks(int max_len);
+int64_t decode_launches(int64_t n_seqs, int64_t n_chunks, int hk);  // 0: one sequence's waves overfill a grid
 int decode_chunk_keys();  // keys per wave
 hipError_t launch_decode_scores(const DecodeArgs& a, int dtype, int head_dim, int group, hipStream_t st);
 

@@ -190,6 +190,15 @@ __device__ __forceinline__ float rope_angle_f32(int p, float w) {
     return (float)p * w;
 }
 
+// An fp64 constant handed to an FMA from scalar registers.  Left to itself the
+// compiler keeps the polynomial coefficients below in vector registers for the
+// whole kernel (two per coefficient) and copies each one before every
+// accumulate-form FMA; read from scalar registers they cost neither.
+__device__ __forceinline__ double sreg(double c) {
+    asm volatile("" : "+s"(c));
+    return c;
+}
+
 // sin and cos, in fp64, of an fp32 angle with |alpha| <= 2^24 (every RoPE
 // angle p * freq with p < 2^24 and freq <= 1; also the pair angles).
 // Cody-Waite reduction by pi/2 (n = nearest integer to alpha * 2/pi, then
@@ -207,24 +216,24 @@ __device__ __forceinline__ void sincos_f64_of_f32(float alpha, double& s_out, do
     r = fma(-n, kPio2Lo, r);
     const double z = r * r;
     // sin r = r + r z (-1/3! + z (1/5! + z (-1/7! + ...)))
-    double ps = 1.0 / 355687428096000.0;                 // 1/17!
-    ps = fma(ps, z, -1.0 / 1307674368000.0);            // 1/15!
-    ps = fma(ps, z, 1.0 / 6227020800.0);                // 1/13!
-    ps = fma(ps, z, -1.0 / 39916800.0);                 // 1/11!
-    ps = fma(ps, z, 1.0 / 362880.0);                    // 1/9!
-    ps = fma(ps, z, -1.0 / 5040.0);                     // 1/7!
-    ps = fma(ps, z, 1.0 / 120.0);                       // 1/5!
-    ps = fma(ps, z, -1.0 / 6.0);                        // 1/3!
+    double ps = 1.0 / 355687428096000.0;            // 1/17!
+    ps = fma(ps, z, sreg(-1.0 / 1307674368000.0));  // 1/15!
+    ps = fma(ps, z, sreg(1.0 / 6227020800.0));      // 1/13!
+    ps = fma(ps, z, sreg(-1.0 / 39916800.0));       // 1/11!
+    ps = fma(ps, z, sreg(1.0 / 362880.0));          // 1/9!
+    ps = fma(ps, z, sreg(-1.0 / 5040.0));           // 1/7!
+    ps = fma(ps, z, sreg(1.0 / 120.0));             // 1/5!
+    ps = fma(ps, z, sreg(-1.0 / 6.0));              // 1/3!
     const double sr = fma(r * z, ps, r);
     // cos r = 1 + z (-1/2! + z (1/4! + z (-1/6! + ...)))
-    double pc = 1.0 / 20922789888000.0;                 // 1/16!
-    pc = fma(pc, z, -1.0 / 87178291200.0);              // 1/14!
-    pc = fma(pc, z, 1.0 / 479001600.0);                 // 1/12!
-    pc = fma(pc, z, -1.0 / 3628800.0);                  // 1/10!
-    pc = fma(pc, z, 1.0 / 40320.0);                     // 1/8!
-    pc = fma(pc, z, -1.0 / 720.0);                      // 1/6!
-    pc = fma(pc, z, 1.0 / 24.0);                        // 1/4!
-    pc = fma(pc, z, -0.5);                              // 1/2!
+    double pc = 1.0 / 20922789888000.0;             // 1/16!
+    pc = fma(pc, z, sreg(-1.0 / 87178291200.0));    // 1/14!
+    pc = fma(pc, z, sreg(1.0 / 479001600.0));       // 1/12!
+    pc = fma(pc, z, sreg(-1.0 / 3628800.0));        // 1/10!
+    pc = fma(pc, z, sreg(1.0 / 40320.0));           // 1/8!
+    pc = fma(pc, z, sreg(-1.0 / 720.0));            // 1/6!
+    pc = fma(pc, z, sreg(1.0 / 24.0));              // 1/4!
+    pc = fma(pc, z, -0.5);                          // 1/2!
     const double cr = fma(z, pc, 1.0);
     const int q = (int)n & 3;
     double sv = (q & 1) ? cr : sr;

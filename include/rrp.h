@@ -133,7 +133,8 @@ typedef struct rrp_shape {
  * k_scale_f32   optional fp32 group scales s32 indexed by TOKEN (not slot),
  *               [n_tokens][n_kv_heads][head_dim/group], 4-byte aligned.
  * stream        hipStream_t or NULL.
- * n_tokens == 0 is a no-op returning RRP_OK. */
+ * n_tokens == 0 is a no-op returning RRP_OK once the shape, support_b and
+ * group are valid; the arrays are then not examined and may be NULL. */
 int rrp_rotate_quantize_qk(const rrp_shape* shape, int32_t dtype, const void* q, const void* k,
                            const int32_t* pos, int64_t n_tokens, const float* angles,
                            int32_t support_b, int32_t group, void* q_out, uint8_t* k_codes,

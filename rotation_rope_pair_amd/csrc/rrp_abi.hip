@@ -112,6 +112,7 @@ int rotate_quantize(const rrp_shape* shape, int32_t dtype, const void* q, const 
     if (st != RRP_OK) return st;
     if ((st = check_b_g(shape, support_b, group)) != RRP_OK) return st;
     if (n_tokens < 0 || n_slots < 0) return RRP_ERR_INVALID_ARG;
+    if (n_tokens == 0) return RRP_OK;  // nothing is read or written; empty arrays may be NULL
     if (k == nullptr || pos == nullptr || k_codes == nullptr || k_scales == nullptr) return RRP_ERR_INVALID_ARG;
     if ((q_out != nullptr || q_rot_f32 != nullptr) && q == nullptr) return RRP_ERR_INVALID_ARG;
     if (slot_mapping == nullptr && n_slots < n_tokens) return RRP_ERR_INVALID_ARG;
@@ -122,7 +123,6 @@ int rotate_quantize(const rrp_shape* shape, int32_t dtype, const void* q, const 
         !aligned(v, 16) || !aligned(v_codes, code_align) || !aligned(v_scales, 2) || !aligned(v_rot_f32, 16) ||
         !aligned(v_scale_f32, 4))
         return RRP_ERR_MISALIGNED;
-    if (n_tokens == 0) return RRP_OK;
 
     rrp::RotateArgs a{};
     a.q = q;

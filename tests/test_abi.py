@@ -69,6 +69,8 @@ def rot(lib, shape=None, dtype=1, q=None, k=P16, pos=P16, T=4, angles=None, b=12
 
 def test_rotate_validation(lib):
     assert rot(lib, T=0, n_slots=0) == 0                          # empty batch: no-op
+    assert rot(lib, T=0, n_slots=0, k=None, pos=None, codes=None, scales=None) == 0  # empty arrays may be NULL
+    assert rot(lib, T=0, b=3) == 1                                # but the call itself is still checked
     assert lib.rrp_rotate_quantize_qk(None, 1, None, P16, P16, 4, None, 128, 128, None, P16, P16, None, 4,
                                       None, None, None, None) == 1
     assert rot(lib, dtype=7) == 1

@@ -841,6 +841,71 @@ def test_diagnostics_parity_degenerate_rows(n, regime):
             assert np.all(rel <= STAT_TOL), (g, b, sw[j], ref, rel)
 
 
+@pytest.mark.parametrize("ah", [0, 8])
+def test_empty_batches_every_entry_point(ah):
+    """No tokens (or no sequences, or only empty sequences): every entry point
+    returns without error and writes only what its definition fixes for an
+    empty batch.
+    - rotate leaves the cache and the query outputs untouched;
+    - calibration leaves the moments as they were and finalises the angles
+      from them;
+    - the diagnostics and the sweep equal the oracle's empty-batch statistics
+      (zeros, and the sweep's support b in field 7);
+    - decode writes no logit."""
+    w = W.WORKLOADS[3]
+    d, hq, hk, g = w.head_dim, w.n_q_heads, w.n_kv_heads, w.group
+    shp = shape_of(w, ah=ah)
+    e = torch.empty((0, hq, d), dtype=torch.bfloat16, device=DEV)
+    ek = torch.empty((0, hk, d), dtype=torch.bfloat16, device=DEV)
+    ep = torch.empty((0,), dtype=torch.int32, device=DEV)
+    ang_np = random_angle_sets(w, 3300) if ah else random_angles(w.n_pairs, 3300)
+    ang = to_dev(ang_np)
+    codes, scales = rrp.new_kv4_cache(16, hk, d, g, DEV)
+    codes.fill_(0x5A)
+    scales.view(torch.int16).fill_(0x1234)
+    rrp.rotate_quantize_qk(shp, e, ek, ep, support_b=d, group=g, k_codes=codes, k_scales=scales, angles=ang,
+                           q_out=torch.empty_like(e), n_slots=16)
+    torch.cuda.synchronize()
+    assert bool((codes == 0x5A).all()) and bool((scales.view(torch.int16) == 0x1234).all())
+
+    # calibration: moments carried in from an earlier batch stay; the angles follow from them
+    inp = inputs(3)
+    q0, k0, p0 = inp["q"][:64], inp["k"][:64], inp["pos"][:64]
+    mom_prev, _ = run_calib(w, q0, k0, p0, "default", ah=ah)
+    mom = torch.from_numpy(mom_prev).to(DEV)
+    A = max(ah, 1)
+    ang_out = torch.empty((d // 2,) if A == 1 else (A, d // 2), dtype=torch.float32, device=DEV)
+    rrp.calibrate_angles(shp, e, ek, ep, moments=mom, estimator="default", angles_out=ang_out)
+    torch.cuda.synchronize()
+    assert np.array_equal(mom.cpu().numpy(), mom_prev)
+    phi64, _, abc = O.angles_from_moments(mom_prev, O.EST_DEFAULT)
+    C.compare_angles(ang_out.cpu().numpy().reshape(-1), phi64.reshape(-1), abc.reshape(-1, 3))
+
+    oshp = oshape_of(w, ah=ah)
+    empty_k = np.zeros((0, hk, d), np.uint16)
+    empty_p = np.zeros((0,), np.int32)
+    st = torch.full((8,), -1.0, dtype=torch.float64, device=DEV)
+    rrp.quant_error_stats(shp, ek, ep, support_b=16, group=g, stats_out=st, angles=ang)
+    sups = rrp.sweep_supports(d)
+    sw = torch.full((len(sups), 8), -1.0, dtype=torch.float64, device=DEV)
+    rrp.quant_error_sweep(shp, ek, ep, group=g, stats_out=sw, angles=ang)
+    torch.cuda.synchronize()
+    assert np.array_equal(st.cpu().numpy(), O.quant_error_stats(oshp, empty_k, empty_p, ang_np, 16, g))
+    ref = np.stack([O.quant_error_stats(oshp, empty_k, empty_p, ang_np, b, g) for b in sups])
+    ref[:, 7] = sups
+    assert np.array_equal(sw.cpu().numpy(), ref)
+
+    # decode: no sequences, then sequences that are all empty
+    for lens in ([], [0, 0, 0]):
+        B = len(lens)
+        out = torch.full((B, hq, 8), float("-inf"), dtype=torch.float32, device=DEV)
+        rrp.decode_scores(shape_of(w), torch.zeros((B, hq, d), dtype=torch.bfloat16, device=DEV), codes, scales,
+                          group=g, seq_start=torch.zeros(B, dtype=torch.int64, device=DEV),
+                          seq_len=torch.tensor(lens, dtype=torch.int32, device=DEV), max_len=8, scores=out)
+        torch.cuda.synchronize()
+        assert bool(torch.isneginf(out).all())
+
+
 def long_inputs(n, T):
     key = ("long", n, T)
     if key not in _INPUTS:

@@ -58,7 +58,10 @@ __device__ __forceinline__ int cslot(int k) { return k + (k >> 2); }
 template <int P> constexpr int ctab_slots() { return P + P / 4; }
 
 // MAXP: row passes loaded per step (a step is double-buffered across tokens).
-template <typename E, int D, int LAYOUT, int MAXP>
+// WHOLE: both streams' head counts are multiples of RP, so every pass holds RP
+// rows.  No lane is then masked: a pass's rows sit at offsets fixed per lane
+// from a wave-uniform base, and the accumulation needs no row test.
+template <typename E, int D, int LAYOUT, int MAXP, bool WHOLE>
 __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
     constexpr int P = D / 2;
     constexpr int LP = P / kCP;  // lanes per row
@@ -103,7 +106,23 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
         for (int m = 0; m < kNSum; ++m) acc[j][m] = 0.0;
 
     const int64_t stride = (int64_t)nb * nwave;
+    unsigned loff[MAXP][2];  // WHOLE: byte offsets of the lane's quads in pass i of a step
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) {
+        loff[i][0] = (unsigned)((i * RP + grp) * ROWB + off0 * EB);
+        loff[i][1] = (unsigned)((i * RP + grp) * ROWB + off1 * EB);
+    }
     auto load_step = [&](int64_t t, int st, QT (&raw)[MAXP][2]) {
+        if constexpr (WHOLE) {
+            const unsigned char* base = src + ((size_t)t * nh_all + h0 + (size_t)st * MAXP * RP) * ROWB;
+#pragma unroll
+            for (int i = 0; i < MAXP; ++i) {
+                if (st * MAXP + i >= npass) continue;  // uniform
+                raw[i][0] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(base + loff[i][0]));
+                raw[i][1] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(base + loff[i][1]));
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < MAXP; ++i) {
             const int row = (st * MAXP + i) * RP + grp;
@@ -154,7 +173,7 @@ __global__ __launch_bounds__(256) void calib_moments_kernel(const CalibArgs a) {
 #pragma unroll
         for (int i = 0; i < MAXP; ++i) {
             const int row = (st * MAXP + i) * RP + grp;
-            if (!(st * MAXP + i < npass && row < nh)) continue;
+            if (!(st * MAXP + i < npass && (WHOLE || row < nh))) continue;
             float x0[4], x1[4];
             Quad<E>::unpack(cur[i][0], x0);
             Quad<E>::unpack(cur[i][1], x1);
@@ -489,7 +508,13 @@ hipError_t launch_t(const CalibArgs& a, hipStream_t st) {
         return hipGetLastError();
     }
     const int blocks = a.nbq + a.nbk;
-    hipLaunchKernelGGL((calib_moments_kernel<E, D, LAYOUT, kCalibMaxPasses>), dim3(blocks), dim3(256), 0, st, a);
+    constexpr int RP = 64 / (D / 2 / kCP);  // rows per pass
+    if ((a.nbq == 0 || a.hq % RP == 0) && a.hk % RP == 0)
+        hipLaunchKernelGGL((calib_moments_kernel<E, D, LAYOUT, kCalibMaxPasses, true>), dim3(blocks), dim3(256), 0,
+                           st, a);
+    else
+        hipLaunchKernelGGL((calib_moments_kernel<E, D, LAYOUT, kCalibMaxPasses, false>), dim3(blocks), dim3(256), 0,
+                           st, a);
     return hipGetLastError();
 }
 

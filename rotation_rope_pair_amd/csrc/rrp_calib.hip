@@ -253,7 +253,12 @@ __host__ __device__ inline int set_group_tokens(int heads, int rows_per_pass) {
     return tg;
 }
 
-template <typename E, int D, int LAYOUT, int MAXP>
+// WHOLE: for both streams the heads per set divide the rows per pass, or the
+// rows per pass divide them, and every token group is full.  A pass then
+// starts at a row whose (token, head) is the same for every lane up to a
+// per-lane constant: the rows are loaded from a wave-uniform base (a scalar
+// cursor) plus fixed per-lane offsets, with no row test.
+template <typename E, int D, int LAYOUT, int MAXP, bool WHOLE>
 __global__ __launch_bounds__(64 * kSetWaves)
 __attribute__((amdgpu_waves_per_eu(std::is_same<E, bf16_tag>::value ? 4 : 1)))  // bf16 fits 128 VGPRs
 void calib_sets_kernel(const CalibArgs a) {
@@ -307,13 +312,37 @@ void calib_sets_kernel(const CalibArgs a) {
     const int qrp = RP / g, rrp = RP % g;
     const int j_first = grp / g, h_first = grp % g;
     int lj = j_first, lh = h_first;  // the next pass to load
+    int uj = 0, uh = 0;              // WHOLE: the same for the pass's first row (wave-uniform)
+    const unsigned lconst0 = (unsigned)((j_first * nh_all + h_first) * ROWB + off0 * EB);
+    const unsigned lconst1 = (unsigned)((j_first * nh_all + h_first) * ROWB + off1 * EB);
     auto load_step = [&](int64_t grp_t, int st, QT (&raw)[MAXP][2], int (&rj)[MAXP]) {
         if (st == 0) {
             lj = j_first;
             lh = h_first;
+            uj = uh = 0;
         }
         const unsigned char* gbase = src + ((size_t)grp_t * tg * nh_all + h0) * ROWB;
         const int64_t tleft = a.n_tokens - grp_t * tg;  // tokens of the group that exist
+        if constexpr (WHOLE) {
+#pragma unroll
+            for (int i = 0; i < MAXP; ++i) {
+                if (active && st * MAXP + i < npass) {  // uniform
+                    const unsigned char* pb = gbase + (size_t)(uj * nh_all + uh) * ROWB;
+                    raw[i][0] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(pb + lconst0));
+                    raw[i][1] = __builtin_nontemporal_load(reinterpret_cast<const QT*>(pb + lconst1));
+                    rj[i] = uj + j_first;
+                } else {
+                    rj[i] = -1;
+                }
+                uh += rrp;
+                uj += qrp;
+                if (uh >= g) {
+                    uh -= g;
+                    ++uj;
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < MAXP; ++i) {
             const bool ok = active && lj < tg && lj < tleft;
@@ -503,8 +532,18 @@ hipError_t launch_t(const CalibArgs& a, hipStream_t st) {
     if (a.n_sets > 1) {
         const int groups = (a.n_sets + kSetWaves - 1) / kSetWaves;
         const int blocks = (a.nbq + a.nbk) * groups;
-        hipLaunchKernelGGL((calib_sets_kernel<E, D, LAYOUT, kCalibMaxPasses>), dim3(blocks), dim3(64 * kSetWaves), 0,
-                           st, a);
+        constexpr int RP = 64 / (D / 2 / kCP);  // rows per pass
+        auto aligned_heads = [&](int heads) {
+            const int g = heads / a.n_sets;
+            return g > 0 && (RP % g == 0 || g % RP == 0) && set_group_tokens(g, RP) * g % RP == 0;
+        };
+        auto full_groups = [&](int heads) { return a.n_tokens % set_group_tokens(heads / a.n_sets, RP) == 0; };
+        if ((a.nbq == 0 || (aligned_heads(a.hq) && full_groups(a.hq))) && aligned_heads(a.hk) && full_groups(a.hk))
+            hipLaunchKernelGGL((calib_sets_kernel<E, D, LAYOUT, kCalibMaxPasses, true>), dim3(blocks),
+                               dim3(64 * kSetWaves), 0, st, a);
+        else
+            hipLaunchKernelGGL((calib_sets_kernel<E, D, LAYOUT, kCalibMaxPasses, false>), dim3(blocks),
+                               dim3(64 * kSetWaves), 0, st, a);
         return hipGetLastError();
     }
     const int blocks = a.nbq + a.nbk;

@@ -332,9 +332,14 @@ void rotate_quantize_kernel(const RotateArgs a) {
 // split over up to kSmallBatchWaves / T waves, at most one pass each, so a
 // decode batch is not serialised on one wave per token).
 constexpr int kSmallBatchWaves = 4096;
-// Grid cap of the large-batch family: waves then walk several tokens each
-// (caps of 2K, 4K, 16K and 32K blocks measured slower at the 128K prefill).
+// Grid caps of the large-batch family; past them waves walk several tokens each.
+// Q/K with shared angles: 32K blocks of 4 waves, one token per wave up to 128K
+// tokens, so the running waves sweep the batch in token order (at the 128K
+// prefill 428 us, against 432 us at 8K blocks and 441 us at 4K).  With V rows
+// or per-set angles, a token is more work and 8K blocks measured best (32K:
+// 0.534 against 0.515 ms with V; 530 against 483 us per set).
 constexpr int64_t kMaxRotateBlocks = 8192;
+constexpr int64_t kMaxRotateBlocksQK = 32768;
 
 template <typename E, int D, int LAYOUT, bool SPLIT>
 hipError_t launch_t(const RotateArgs& args, hipStream_t st) {
@@ -352,7 +357,8 @@ hipError_t launch_t(const RotateArgs& args, hipStream_t st) {
         a.split = split < 1 ? 1 : (int)split;
     }
     int64_t blocks = (a.n_tokens * a.split + wpb - 1) / wpb;
-    if (blocks > kMaxRotateBlocks) blocks = kMaxRotateBlocks;
+    const int64_t cap = (!SPLIT && !ph && a.v == nullptr) ? kMaxRotateBlocksQK : kMaxRotateBlocks;
+    if (blocks > cap) blocks = cap;
     const bool smallg = a.group < Geo<E, D>::CE;
     const dim3 grid((unsigned)blocks), block(64 * wpb);
 #define RRP_LAUNCH(SG, BT, HV, PHV) \

@@ -81,6 +81,17 @@ __device__ __forceinline__ void load_row_chunks(const unsigned char* __restrict_
         r[ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + chunk_offset<E, D>(ch, s_src)));
 }
 
+// Direct global -> LDS loads of one row pass (gfx950 global_load_lds_dwordx4):
+// lane i's 16 bytes of chunk ch land at dst[ch][i].  The data holds no VGPRs
+// while in flight; the caller waits on vmcnt before reading dst.
+template <typename E, int D>
+__device__ __forceinline__ void stage_row_chunks(const unsigned char* __restrict__ row, int s_src, u32x4 (*dst)[64]) {
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(row + chunk_offset<E, D>(ch, s_src)),
+                                         (__attribute__((address_space(3))) void*)(dst[ch]), 16, 0, 0);
+}
+
 // Row passes kept in flight per token: one Q pass (two Q passes measured
 // slower: 155 instead of 136 VGPRs, two instead of three waves per SIMD) and
 // one K pass (two when a pass holds fewer than 8 rows).
@@ -99,6 +110,8 @@ template <int R> struct Depth {
 // (9 KB), blocks of kPerSetWaves = 4 waves take 46 KB, three per CU.
 // SPLIT: each token's row passes are shared by a.split waves (small batches).
 constexpr int kPerSetWaves = 4;
+// Q passes staged through LDS per token (after the first, which goes to VGPRs).
+constexpr int kStagedQPasses = 3;
 
 template <typename E, int D, int LAYOUT, bool SMALLG, int BT, bool HAS_V, bool PH, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, PH ? 64 * kPerSetWaves : 256)))
@@ -109,11 +122,18 @@ void rotate_quantize_kernel(const RotateArgs a) {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr int ROWB = D * EB;
     constexpr int MQ = Depth<R>::Q, MK = Depth<R>::K;
+    static_assert(MQ == 1 || SPLIT || PH || HAS_V, "Q staging assumes one Q pass in flight");
     constexpr bool FOLD = (LAYOUT == 0) && (BT == D);
     constexpr int WMAX = PH ? kPerSetWaves : 4;  // waves per block
     __shared__ float2 tab32_all[WMAX][PH ? 1 : tab_entries<P>()];
     __shared__ double2 tab64_all[WMAX][PH ? kSetStride * P : tab_entries<P>()];
     __shared__ double2 phi_all[PH ? kSetStride * P : 1];
+    // STAGE (Q/K with shared angles, one token per wave): the token's Q passes
+    // after the first go straight to LDS at the token's start, so every row of
+    // the token is in flight at once without holding VGPRs.
+    constexpr bool STAGE = !SPLIT && !PH && !HAS_V;
+    constexpr int NS = STAGE ? kStagedQPasses : 1;
+    __shared__ u32x4 stage_all[STAGE ? WMAX : 1][NS][2][64];
 
     const int lane = (int)__lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -127,6 +147,7 @@ void rotate_quantize_kernel(const RotateArgs a) {
     if constexpr (PH) load_angle_sets<P>(phi_all, a.angles, a.angle_sets);
     else if (a.angles != nullptr && lane < P) sincos_f64_of_f32(a.angles[lane], sphi, cphi);
     const float invf = lane < P ? a.inv_freq[lane] : 0.0f;
+    if constexpr (STAGE) asm volatile("" ::"v"(invf), "v"(cphi), "v"(sphi));  // retired before the first row loads
     // Rows are loaded permuted (lane s holds position s ^ perm), see fwht_row.
     const int s_src = s ^ lane_perm_mask<D, CE>(BT ? BT : a.support_b);
     const int s_src_v = s ^ lane_perm_mask<D, CE>(D);  // V: full-head support
@@ -169,9 +190,6 @@ void rotate_quantize_kernel(const RotateArgs a) {
             v0 = min(max(u0 - nq - nk, 0), nk);
             v1 = min(max(u1 - nq - nk, 0), nk);
         }
-        const int p = a.pos[t];
-        const int64_t slot = a.slot_mapping ? a.slot_mapping[t] : t;
-        const bool in_cache = slot >= 0 && slot < a.n_slots;
         // wave-uniform row bases of this token
         const unsigned char* qt = qb + (size_t)t * a.hq * ROWB;
         const unsigned char* kt = kb + (size_t)t * hk * ROWB;
@@ -194,14 +212,40 @@ void rotate_quantize_kernel(const RotateArgs a) {
                 if (v0 + i < v1 && (v0 + i) * R + grp < hk)
                     load_row_chunks<E, D>(vt + (v0 + i) * R * ROWB + ld_off, s_src_v, rv[i]);
         }
+        // Q passes q0 + 1 .. q0 + ns go to LDS (STAGE only).
+        int ns = 0;
+        if constexpr (STAGE) {
+            ns = min(q1 - q0 - 1, NS);
+            // the previous token's reads of the staging buffer have returned
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                if (i < ns && (q0 + 1 + i) * R + grp < hq)
+                    stage_row_chunks<E, D>(qt + (q0 + 1 + i) * R * ROWB + ld_off, s_src, stage_all[wave][i]);
+            asm volatile("" ::: "memory");  // issue order: before the table build and the first stores
+        }
+        // Position and slot after the row loads: the first wait on them then
+        // covers the rows too, and no row load waits for them.
+        const int p = a.pos[t];
+        const int64_t slot = a.slot_mapping ? a.slot_mapping[t] : t;
+        const bool in_cache = slot >= 0 && slot < a.n_slots;
 
         if constexpr (PH)
             token_tables_sets<D, FOLD>(nullptr, tab64, lane, p, invf, phi_all, a.angle_sets, a.rsqrt_b);
         else token_tables<D, FOLD>(tab32, tab64, lane, p, invf, cphi, sphi, a.rsqrt_b);
+        // The staged passes have landed.  The table build has already waited
+        // for the position, issued after them, so this adds no wait of its own.
+        if (STAGE && ns > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
         // ---- Q rows (fp32) ----
         for (int c0 = q0; c0 < q1; c0 += MQ) {
-            if (c0 > q0) {
+            const int si = c0 - q0 - 1;  // staging slot of this pass (STAGE, MQ == 1)
+            if (STAGE && si >= 0 && si < ns) {
+                if (c0 * R + grp < hq) {
+                    rq[0][0] = stage_all[wave][si][0][lane];
+                    rq[0][1] = stage_all[wave][si][1][lane];
+                }
+            } else if (c0 > q0) {
 #pragma unroll
                 for (int i = 0; i < MQ; ++i)
                     if (c0 + i < q1 && (c0 + i) * R + grp < hq)

@@ -413,14 +413,16 @@ RRP_EXPORT int rrp_decode_scores(const rrp_shape* shape, int32_t dtype, const vo
     const int hq = shape->n_q_heads, hk = shape->n_kv_heads, d = shape->head_dim;
     if (hq < 1 || hq % hk != 0) return RRP_ERR_INVALID_ARG;
     if (hq / hk > 16) return RRP_ERR_UNSUPPORTED;  // one MFMA column per query head of a key head
-    // a wave's chunk of keys is addressed by 32-bit offsets from its first row
-    if ((int64_t)rrp::decode_chunk_keys() * hk * (d / 2) >= ((int64_t)1 << 31)) return RRP_ERR_UNSUPPORTED;
+    // A wave's chunk of keys is addressed by 32-bit offsets from its first row.
+    // The stated bounds hold for a band of 256 keys, which covers the chunk.
+    const int64_t band = rrp::decode_chunk_keys() > 256 ? rrp::decode_chunk_keys() : 256;
+    if (band * hk * (d / 2) >= ((int64_t)1 << 31)) return RRP_ERR_UNSUPPORTED;
     if (!is_pow2(group) || group < 2 || group > d) return RRP_ERR_INVALID_ARG;
     if (n_seqs < 0 || n_slots < 0 || max_len < 0) return RRP_ERR_INVALID_ARG;
     if (n_seqs == 0 || max_len == 0) return RRP_OK;
     if (n_slots == 0) return RRP_ERR_INVALID_ARG;  // an empty cache holds no key to read
     // key indices are 32-bit: a chunk's end plus one tile stays below 2^31
-    if (max_len > INT32_MAX - 2 * rrp::decode_chunk_keys()) return RRP_ERR_UNSUPPORTED;
+    if (max_len > INT32_MAX - 2 * band) return RRP_ERR_UNSUPPORTED;
     if (q == nullptr || k_codes == nullptr || k_scales == nullptr || seq_start == nullptr || seq_len == nullptr ||
         scores == nullptr)
         return RRP_ERR_INVALID_ARG;

@@ -35,8 +35,11 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// Keys per wave (one chunk): chunks of 128 keys measured the same, 512 slower.
-constexpr int kKeysPerWave = 256;
+// Keys per wave (one chunk).  With the chunk staged through LDS (8.5 KB per
+// wave at 128 keys, four waves per SIMD) 128 keys measured 0.564 ms on the
+// 256-sequence decode batch; 256 keys (17 KB per wave, two waves per SIMD)
+// 0.664 ms.  Before staging, 128 and 256 measured the same and 512 slower.
+constexpr int kKeysPerWave = 128;
 // 16-key tiles loaded per step: one (66 VGPRs, 7 waves per SIMD) measured
 // faster than two (104 VGPRs, 4 waves per SIMD).
 constexpr int kTilesPerStep = 1;
@@ -138,6 +141,14 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
     constexpr bool SWAP = KBM && NG == 2;
     constexpr int LSPAN = D / 4;                // channels per lane block (kb-major)
     constexpr int KPG = KBM ? GS / LSPAN : 1;   // lane blocks per group (kb-major)
+
+    // STAGE (d = 128, two groups per row: 4-byte scale rows): a wave's whole
+    // chunk of codes and scales goes straight to LDS with direct loads at its
+    // start, so all of it is in flight at once without holding VGPRs.
+    constexpr bool STAGE = KBM && NM == 4 && SROW == 4 && kTilesPerStep == 1;
+    constexpr int NT = kKeysPerWave / 16;  // tiles per chunk
+    __shared__ u32x4 st_codes[STAGE ? 4 : 1][STAGE ? NT : 1][64];
+    __shared__ __attribute__((aligned(16))) unsigned st_scales[STAGE ? 4 : 1][STAGE ? kKeysPerWave : 1];
 
     const int lane = (int)__lane_id();
     // wave-uniform (scalar) indices, so row bases stay in scalar registers
@@ -334,35 +345,59 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
             }
             load_step(s0, w, sw);
         };
-        load_any(k_begin, wc, sc);  // the first codes are in flight while the queries are prepared
+        constexpr bool DMA = STAGE && FAST;
+        if constexpr (DMA) {
+            // Codes: tile tt's load puts lane (col, kb)'s 16 bytes (key k_begin +
+            // 16 tt + col, bytes 16 kb of its row) at st_codes[wave][tt][lane].
+            // Scales: lane i of load j puts key k_begin + 64 j + i's scale row at
+            // st_scales[wave][64 j + i].  Keys past the chunk's end read its last key.
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+                if (k_begin + 16 * tt < k_end) {
+                    const unsigned kc = (unsigned)(min(k_begin + 16 * tt + col, k_end - 1) - k_begin);
+                    __builtin_amdgcn_global_load_lds(
+                        static_cast<const void*>(cbase + (size_t)(kc * (unsigned)slot_stride_c + lane_c)),
+                        (__attribute__((address_space(3))) void*)st_codes[wave][tt], 16, 0, 0);
+                }
+#pragma unroll
+            for (int j = 0; j < kKeysPerWave / 64; ++j)
+                if (k_begin + 64 * j < k_end) {
+                    const unsigned kc = (unsigned)(min(k_begin + 64 * j + lane, k_end - 1) - k_begin);
+                    __builtin_amdgcn_global_load_lds(
+                        static_cast<const void*>(sbase + (size_t)(kc * (unsigned)slot_stride_s)),
+                        (__attribute__((address_space(3))) void*)&st_scales[wave][64 * j], 4, 0, 0);
+                }
+            asm volatile("" ::: "memory");  // issued before the query loads
+        } else {
+            load_any(k_begin, wc, sc);  // the first codes are in flight while the queries are prepared
+        }
 
         // ---- B operand: this lane's query channels (kb-major: LSPAN kb + 8 m + elem_channel(e);
         //      m-major: 32 m + 8 kb + elem_channel(e)) ----
+        // Every lane loads, so the loads need no branch: a lane past the group's
+        // query heads (col >= G) reads the group's first head and zeroes what it
+        // read.  (Loads inside a divergent branch each waited for their data
+        // before the branch joined.)
         float qv[NM][8];
         float qmax = 0.0f;
+        const void* qrow = static_cast<const unsigned char*>(a.q) +
+                           ((size_t)b * a.hq + (head_ok ? h : kvh * G)) * D * ElemInfo<E>::bytes;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             float x[8];
-            if (head_ok) {
-                const void* row = static_cast<const unsigned char*>(a.q) +
-                                  ((size_t)b * a.hq + h) * D * ElemInfo<E>::bytes;
-                int c0;
-                if constexpr (SWAP) {
-                    // operand m = 2i (group 0) / 2i + 1 (group 1) after the half-wave swap
-                    const int i = m >> 1;
-                    if ((m & 1) == 0) c0 = kb < 2 ? LSPAN * kb + 16 * i : LSPAN * (kb - 2) + 16 * i + 8;
-                    else c0 = kb < 2 ? LSPAN * (kb + 2) + 16 * i : LSPAN * kb + 16 * i + 8;
-                } else {
-                    c0 = KBM ? LSPAN * kb + 8 * m : 32 * m + 8 * kb;
-                }
-                QLoad<E>::load(row, c0, x);
+            int c0;
+            if constexpr (SWAP) {
+                // operand m = 2i (group 0) / 2i + 1 (group 1) after the half-wave swap
+                const int i = m >> 1;
+                if ((m & 1) == 0) c0 = kb < 2 ? LSPAN * kb + 16 * i : LSPAN * (kb - 2) + 16 * i + 8;
+                else c0 = kb < 2 ? LSPAN * (kb + 2) + 16 * i : LSPAN * kb + 16 * i + 8;
             } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+                c0 = KBM ? LSPAN * kb + 8 * m : 32 * m + 8 * kb;
             }
+            QLoad<E>::load(qrow, c0, x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                qv[m][e] = x[elem_channel(e)];
+                qv[m][e] = head_ok ? x[elem_channel(e)] : 0.0f;
                 qmax = fmaxf(qmax, fabsf(qv[m][e]));
             }
         }
@@ -490,6 +525,22 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
             }
         };
 
+        if constexpr (DMA) {
+            // The staged chunk has landed (the query loads, issued after it, were
+            // waited for by the query preparation already).
+            wait_vm_all();
+            for (int tt = 0; tt < NT && k_begin + 16 * tt < k_end; ++tt) {
+                const u32x4 v = st_codes[wave][tt][lane];
+                const u32x4 sv = *reinterpret_cast<const u32x4*>(&st_scales[wave][16 * tt + 4 * kb]);
+                unsigned w4[NM], s4[4][NSW];
+#pragma unroll
+                for (int m = 0; m < NM; ++m) w4[m] = v[m];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s4[r][0] = sv[r];
+                tile(k_begin + 16 * tt, w4, s4);
+            }
+            return;
+        }
         // Retire the first step's loads here (the queries were prepared while they
         // were in flight): inside the loop the current step is then always a copy
         // made after its wait, and its first use needs no wait, which would

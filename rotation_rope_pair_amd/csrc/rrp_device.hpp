@@ -22,6 +22,24 @@ namespace rrp {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Wait until every vector memory operation of the wave has completed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt fields left at "no wait").  Issued
+// through the builtin, so the compiler's own wait-count tracking sees it: a
+// direct global -> LDS load waited for here needs no further wait before the
+// LDS reads that follow, even with stores issued in between.  The empty asm
+// keeps memory accesses from moving across the wait.
+__device__ __forceinline__ void wait_vm_all() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+}
+
+// Wait until every vector memory and LDS operation of the wave has completed
+// (vmcnt(0) lgkmcnt(0)), again visible to the compiler's tracking.
+__device__ __forceinline__ void wait_vm_lds_all() {
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("" ::: "memory");
+}
+
 struct bf16_tag {};  // element type marker: bf16 stored as uint16 bit patterns
 
 template <typename E> struct ElemInfo;

@@ -190,6 +190,11 @@ void rotate_quantize_kernel(const RotateArgs a) {
             v0 = min(max(u0 - nq - nk, 0), nk);
             v1 = min(max(u1 - nq - nk, 0), nk);
         }
+        // A wave walking several tokens: the previous token's accesses have
+        // completed (its reads of the staging buffer included), and the
+        // compiler knows it, so no load of this token waits on a register of
+        // the last one.  Free for the first token.
+        if constexpr (STAGE) wait_vm_lds_all();
         // wave-uniform row bases of this token
         const unsigned char* qt = qb + (size_t)t * a.hq * ROWB;
         const unsigned char* kt = kb + (size_t)t * hk * ROWB;
@@ -216,8 +221,6 @@ void rotate_quantize_kernel(const RotateArgs a) {
         int ns = 0;
         if constexpr (STAGE) {
             ns = min(q1 - q0 - 1, NS);
-            // the previous token's reads of the staging buffer have returned
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
             for (int i = 0; i < NS; ++i)
                 if (i < ns && (q0 + 1 + i) * R + grp < hq)
@@ -233,9 +236,10 @@ void rotate_quantize_kernel(const RotateArgs a) {
         if constexpr (PH)
             token_tables_sets<D, FOLD>(nullptr, tab64, lane, p, invf, phi_all, a.angle_sets, a.rsqrt_b);
         else token_tables<D, FOLD>(tab32, tab64, lane, p, invf, cphi, sphi, a.rsqrt_b);
-        // The staged passes have landed.  The table build has already waited
-        // for the position, issued after them, so this adds no wait of its own.
-        if (STAGE && ns > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // Every row of the token has landed.  The table build has already
+        // waited for the position, issued after them, so this adds no wait of
+        // its own; unconditional, so the compiler knows it on every path.
+        if constexpr (STAGE) wait_vm_all();
 
         // ---- Q rows (fp32) ----
         for (int c0 = q0; c0 < q1; c0 += MQ) {

@@ -137,7 +137,7 @@ def test_decode_scores_validation(lib):
     assert dec(scales=ctypes.c_void_p((1 << 20) + 2), g=32) == 2   # 8-byte scale rows need 8-byte alignment
     assert dec(shape=_shape(d=96)) == 3
     assert dec(max_len=2**31 - 1) == 3 and dec(max_len=2**31 - 512) == 3   # key indices stay 32-bit
-    # one sequence's waves (ceil(max_len / 256) * n_kv_heads) overfill a one-dimensional grid
+    # one sequence's waves (ceil(max_len / 128) * n_kv_heads) overfill a one-dimensional grid
     assert dec(shape=_shape(hq=9, hk=9), max_len=2**31 - 1024) == 3
     assert dec(shape=_shape(hq=12, hk=12), max_len=2**31 - 1024) == 3  # over 65535 chunks: no 3-D grid either
 

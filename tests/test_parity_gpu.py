@@ -763,24 +763,30 @@ def test_stats_and_sweep_parity_interleaved_pairs(n, g, ah):
 
 # ---------------------------------------------------------------------------
 # The large-batch kernel family (4096 tokens or more: one wave per token, waves
-# walking the batch with a grid stride of 8192 blocks x 4 waves = 32768 tokens)
-# against the oracle, for every compile-time variant a prefill can reach:
-# runtime support b < d, groups smaller than a 16-byte chunk, interleaved pairs,
-# fp32 rows, head_dim 64, per-key-head angle sets and the V half.  Batches are
-# longer than one grid-stride round, and the sampled tokens include both ends of
-# every round, the last one in particular.
+# walking the batch with a grid stride) against the oracle, for every
+# compile-time variant a prefill can reach: runtime support b < d, groups
+# smaller than a 16-byte chunk, interleaved pairs, fp32 rows, head_dim 64,
+# per-key-head angle sets and the V half.  A grid-stride round is 32768 blocks
+# x 4 waves = 131072 tokens for Q/K launches with shared angles (whose waves
+# stage Q rows through LDS, reused token after token) and 8192 blocks x 4 waves
+# = 32768 tokens with V rows or per-set angles.  Batches are longer than one
+# round of their launch, and the sampled tokens include both ends of every
+# round, the last one in particular.
 # ---------------------------------------------------------------------------
 
-GRID_STRIDE_TOKENS = 8192 * 4  # tokens per grid-stride round of the large-batch family
+GRID_STRIDE_TOKENS = 8192 * 4  # round of the launches with V rows or per-set angles
+GRID_STRIDE_TOKENS_QK = 32768 * 4  # round of the Q/K launches with shared angles
+T_TWO_ROUNDS = GRID_STRIDE_TOKENS_QK + 8192 + 77  # past one shared-angle round, ragged
 
 
 def grid_sample(T, n, seed):
     """n sampled tokens of a T-token batch plus the first and last token of every
-    grid-stride round."""
+    grid-stride round of either launch shape."""
     assert T >= 4096
     edges = []
-    for r0 in range(0, T, GRID_STRIDE_TOKENS):
-        edges += [r0, min(T, r0 + GRID_STRIDE_TOKENS) - 1]
+    for rnd in (GRID_STRIDE_TOKENS, GRID_STRIDE_TOKENS_QK):
+        for r0 in range(0, T, rnd):
+            edges += [r0, min(T, r0 + rnd) - 1]
     return np.unique(np.concatenate([sample_tokens(T, n, seed), np.array(edges)]))
 
 
@@ -916,8 +922,9 @@ def long_inputs(n, T):
 @pytest.mark.parametrize("ah", [0, 8])
 @pytest.mark.parametrize("b", [1, 2, 16, 64])
 def test_grid_stride_prefill_128k_support_sweep(b, ah):
-    """The 131072-token prefill (four grid-stride rounds) at b < d, shared and
-    per-key-head angles, in the benchmark's launch configuration."""
+    """The 131072-token prefill at b < d, shared and per-key-head angles, in the
+    benchmark's launch configuration (one round of the shared-angle launch, four
+    of the per-set launch)."""
     w, inp = W.WORKLOADS[4], inputs(4)
     ang = random_angle_sets(w, 2000 + b) if ah else random_angles(w.n_pairs, 2000 + b)
     out = run_rotate(w, inp, ang, b, 128, debug=False, ah=ah)
@@ -947,10 +954,11 @@ def test_grid_stride_prefill_128k_interleaved_pairs(b, ah):
 
 @pytest.mark.parametrize("b,g,layout", [(2, 64, 0), (64, 64, 0), (8, 2, 0), (32, 16, 1), (1, 64, 1)])
 def test_grid_stride_fp32_rows_tiny_shape(b, g, layout):
-    """fp32 rows of the tiny workload's shape (2 Q / 1 KV heads, d 64) over 40960
-    tokens (two grid-stride rounds), with the fp32 debug copies."""
+    """fp32 rows of the tiny workload's shape (2 Q / 1 KV heads, d 64) over
+    T_TWO_ROUNDS tokens (past one shared-angle round), with the fp32 debug
+    copies."""
     w = W.WORKLOADS[1]
-    T = 40960
+    T = T_TWO_ROUNDS
     inp = long_inputs(1, T)
     ang = random_angles(w.n_pairs, 2300 + b)
     out = run_rotate(w, inp, ang, b, g, layout=layout)
@@ -959,14 +967,29 @@ def test_grid_stride_fp32_rows_tiny_shape(b, g, layout):
 
 @pytest.mark.parametrize("b,g,ah", [(2, 64, 0), (16, 64, 0), (32, 4, 0), (64, 64, 8), (4, 16, 8)])
 def test_grid_stride_head_dim_64(b, g, ah):
-    """head_dim 64 (the 1B layer's 32 / 8 heads) over 40960 tokens, with the fp32
-    debug copies."""
+    """head_dim 64 (the 1B layer's 32 / 8 heads) over T_TWO_ROUNDS tokens (past
+    one shared-angle round), with the fp32 debug copies."""
     w = W.WORKLOADS[2]
-    T = 40960
+    T = T_TWO_ROUNDS
     inp = long_inputs(2, T)
     ang = random_angle_sets(w, 2400 + b) if ah else random_angles(w.n_pairs, 2400 + b)
     out = run_rotate(w, inp, ang, b, g, ah=ah)
     print(b, g, ah, check_rotate(w, inp, out, ang, b, g, grid_sample(T, 768, 2400 + b), ah=ah))
+
+
+@pytest.mark.parametrize("b,g,layout", [(2, 4, 0), (16, 128, 1), (64, 16, 0), (128, 128, 0)])
+def test_grid_stride_two_rounds_shared_angles(b, g, layout):
+    """The 128K prefill's shape over T_TWO_ROUNDS tokens with shared angles: the
+    waves of the first 8269 token slots walk a second token, reusing the LDS
+    buffer their first token's Q rows were staged in."""
+    w = W.WORKLOADS[4]
+    T = T_TWO_ROUNDS
+    inp = long_inputs(4, T)
+    ang = random_angles(w.n_pairs, 2600 + b)
+    out = run_rotate(w, inp, ang, b, g, debug=False, layout=layout)
+    idx = grid_sample(T, 768, 2600 + b + g)
+    assert (idx >= GRID_STRIDE_TOKENS_QK).sum() > 30
+    print(b, g, layout, check_rotate(w, inp, out, ang, b, g, idx, layout=layout))
 
 
 @pytest.mark.parametrize("b,g,ah", [(2, 4, 0), (16, 128, 8)])

@@ -35,11 +35,12 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// Keys per wave (one chunk).  With the chunk staged through LDS (8.5 KB per
-// wave at 128 keys, four waves per SIMD) 128 keys measured 0.564 ms on the
-// 256-sequence decode batch; 256 keys (17 KB per wave, two waves per SIMD)
-// 0.664 ms.  Before staging, 128 and 256 measured the same and 512 slower.
-constexpr int kKeysPerWave = 128;
+// Keys per wave (one chunk).  With the chunk staged through LDS the chunk
+// sets the waves per SIMD: 112 keys (7.5 KB per wave, five waves per SIMD)
+// measured 0.557-0.558 ms on the 256-sequence decode batch, 128 keys (8.5 KB,
+// four) 0.563-0.564 ms, 96 keys 0.561 ms, 64 keys 0.577 ms and 256 keys (17 KB,
+// two) 0.664 ms.  Before staging, 128 and 256 measured the same and 512 slower.
+constexpr int kKeysPerWave = 112;
 // 16-key tiles loaded per step: one (66 VGPRs, 7 waves per SIMD) measured
 // faster than two (104 VGPRs, 4 waves per SIMD).
 constexpr int kTilesPerStep = 1;
@@ -146,9 +147,11 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
     // chunk of codes and scales goes straight to LDS with direct loads at its
     // start, so all of it is in flight at once without holding VGPRs.
     constexpr bool STAGE = KBM && NM == 4 && SROW == 4 && kTilesPerStep == 1;
-    constexpr int NT = kKeysPerWave / 16;  // tiles per chunk
+    constexpr int NT = kKeysPerWave / 16;         // tiles per chunk
+    constexpr int NSL = (kKeysPerWave + 63) / 64;  // scale loads per chunk (64 keys each)
+    static_assert(kKeysPerWave % 16 == 0, "whole tiles per chunk");
     __shared__ u32x4 st_codes[STAGE ? 4 : 1][STAGE ? NT : 1][64];
-    __shared__ __attribute__((aligned(16))) unsigned st_scales[STAGE ? 4 : 1][STAGE ? kKeysPerWave : 1];
+    __shared__ __attribute__((aligned(16))) unsigned st_scales[STAGE ? 4 : 1][STAGE ? 64 * NSL : 1];
 
     const int lane = (int)__lane_id();
     // wave-uniform (scalar) indices, so row bases stay in scalar registers
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(const DecodeArgs a) 
                         (__attribute__((address_space(3))) void*)st_codes[wave][tt], 16, 0, 0);
                 }
 #pragma unroll
-            for (int j = 0; j < kKeysPerWave / 64; ++j)
+            for (int j = 0; j < NSL; ++j)
                 if (k_begin + 64 * j < k_end) {
                     const unsigned kc = (unsigned)(min(k_begin + 64 * j + lane, k_end - 1) - k_begin);
                     __builtin_amdgcn_global_load_lds(

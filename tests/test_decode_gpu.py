@@ -101,10 +101,11 @@ def compare(got, ref, mags, seqs, hq, lens, max_len):
     ("f32", 64, 4, 2, 2)])
 def test_decode_scores_against_oracle_cache(dtype, d, hq, hk, g):
     """Cache and queries written by the oracle's rotate path; ragged lengths across
-    tile and chunk edges, an empty sequence, keys past the cache (NaN), and a row
-    length that is not a multiple of 4."""
+    the edges of 16-key tiles, 64-key scale loads and 112-key chunks (and of the
+    256-key chunks of earlier builds), an empty sequence, keys past the cache
+    (NaN), and a row length that is not a multiple of 4."""
     rng = np.random.Generator(np.random.PCG64(900 + d + hq + g))
-    lens = np.array([0, 1, 15, 16, 17, 255, 256, 257, 600, 37], np.int32)
+    lens = np.array([0, 1, 15, 16, 17, 63, 64, 65, 111, 112, 113, 224, 225, 255, 256, 257, 600, 37], np.int32)
     B, cap = len(lens), 640
     n_slots = B * cap
     start = np.arange(B, dtype=np.int64) * cap

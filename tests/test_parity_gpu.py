@@ -992,6 +992,29 @@ def test_grid_stride_two_rounds_shared_angles(b, g, layout):
     print(b, g, layout, check_rotate(w, inp, out, ang, b, g, idx, layout=layout))
 
 
+@pytest.mark.parametrize("b,g,ah", [(128, 128, 0), (16, 32, 0), (2, 8, 8)])
+def test_grid_stride_many_query_heads(b, g, ah):
+    """64 query heads over 8 key heads (eight Q passes per token): with shared
+    angles the kernel stages Q passes 1-3 through LDS and loads passes 4-7 one
+    ahead into VGPRs.  A ragged batch past one grid-stride round of the
+    shared-angle launch, against the oracle on sampled tokens."""
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS[4], n_q_heads=64, n_tokens=T_TWO_ROUNDS)
+    T = T_TWO_ROUNDS
+    key = ("hq64", T)
+    if key not in _INPUTS:
+        rng = np.random.Generator(np.random.PCG64(2700))
+        scale = rng.lognormal(0.0, 0.7, w.head_dim).astype(np.float32)
+        normal = lambda n: rng.standard_normal((T, n, w.head_dim), dtype=np.float32) * scale  # noqa: E731
+        _INPUTS[key] = {"q": W._to_storage(normal(64), "bf16"), "k": W._to_storage(normal(8), "bf16"),
+                        "pos": np.arange(T, dtype=np.int32)}
+    inp = _INPUTS[key]
+    ang = random_angle_sets(w, 2700 + b) if ah else random_angles(w.n_pairs, 2700 + b)
+    out = run_rotate(w, inp, ang, b, g, debug=False, ah=ah)
+    idx = grid_sample(T, 512, 2700 + b + g)
+    print(b, g, ah, check_rotate(w, inp, out, ang, b, g, idx, ah=ah))
+
+
 @pytest.mark.parametrize("b,g,ah", [(2, 4, 0), (16, 128, 8)])
 def test_grid_stride_prefill_128k_with_v(b, g, ah):
     """The V half at b < d and a small group on the full prefill."""

@@ -92,9 +92,10 @@ __device__ __forceinline__ void stage_row_chunks(const unsigned char* __restrict
                                          (__attribute__((address_space(3))) void*)(dst[ch]), 16, 0, 0);
 }
 
-// Row passes kept in flight per token: one Q pass (two Q passes measured
+// Row passes kept in VGPRs per token: one Q pass (two Q passes measured
 // slower: 155 instead of 136 VGPRs, two instead of three waves per SIMD) and
-// one K pass (two when a pass holds fewer than 8 rows).
+// one K pass (two when a pass holds fewer than 8 rows).  Q/K launches with
+// shared angles also have the next kStagedQPasses Q passes in flight, in LDS.
 template <int R> struct Depth {
     static constexpr int Q = 1;
     static constexpr int K = R >= 8 ? 1 : 2;

@@ -992,21 +992,24 @@ def test_grid_stride_two_rounds_shared_angles(b, g, layout):
     print(b, g, layout, check_rotate(w, inp, out, ang, b, g, idx, layout=layout))
 
 
-@pytest.mark.parametrize("b,g,ah", [(128, 128, 0), (16, 32, 0), (2, 8, 8)])
-def test_grid_stride_many_query_heads(b, g, ah):
-    """64 query heads over 8 key heads (eight Q passes per token): with shared
-    angles the kernel stages Q passes 1-3 through LDS and loads passes 4-7 one
-    ahead into VGPRs.  A ragged batch past one grid-stride round of the
+@pytest.mark.parametrize("hq,hk,b,g,ah", [(64, 8, 128, 128, 0), (64, 8, 16, 32, 0), (64, 8, 2, 8, 8),
+                                          (12, 4, 128, 128, 0), (12, 4, 16, 4, 4)])
+def test_grid_stride_many_query_heads(hq, hk, b, g, ah):
+    """Head counts other than the workloads': 64 query heads over 8 key heads
+    (eight Q passes per token: with shared angles the kernel stages Q passes 1-3
+    through LDS and loads passes 4-7 one ahead into VGPRs), and 12 over 4 (the
+    staged second Q pass and the K pass only half filled: the masked lanes
+    neither load nor store).  A ragged batch past one grid-stride round of the
     shared-angle launch, against the oracle on sampled tokens."""
     import dataclasses
-    w = dataclasses.replace(W.WORKLOADS[4], n_q_heads=64, n_tokens=T_TWO_ROUNDS)
+    w = dataclasses.replace(W.WORKLOADS[4], n_q_heads=hq, n_kv_heads=hk, n_tokens=T_TWO_ROUNDS)
     T = T_TWO_ROUNDS
-    key = ("hq64", T)
+    key = ("heads", hq, hk, T)
     if key not in _INPUTS:
-        rng = np.random.Generator(np.random.PCG64(2700))
+        rng = np.random.Generator(np.random.PCG64(2700 + hq))
         scale = rng.lognormal(0.0, 0.7, w.head_dim).astype(np.float32)
         normal = lambda n: rng.standard_normal((T, n, w.head_dim), dtype=np.float32) * scale  # noqa: E731
-        _INPUTS[key] = {"q": W._to_storage(normal(64), "bf16"), "k": W._to_storage(normal(8), "bf16"),
+        _INPUTS[key] = {"q": W._to_storage(normal(hq), "bf16"), "k": W._to_storage(normal(hk), "bf16"),
                         "pos": np.arange(T, dtype=np.int32)}
     inp = _INPUTS[key]
     ang = random_angle_sets(w, 2700 + b) if ah else random_angles(w.n_pairs, 2700 + b)

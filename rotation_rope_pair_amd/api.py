@@ -39,25 +39,45 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _dev(t: Optional[torch.Tensor], name: str, numel: Optional[int] = None, dtype=None, device=None):
+    """Device pointer (an int; None for an absent tensor) of `t` after the
+    binding's checks: a contiguous device tensor on device ordinal `device`
+    with at least `numel` elements of `dtype` (one dtype or a tuple).  The
+    checks read only the tensor's own fields, so they cost a few hundred ns."""
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if not isinstance(t, torch.Tensor):
         raise ValueError(f"{name} must be a device (cuda) tensor")
+    where = t.get_device()  # -1 for a host tensor
+    if where < 0:
+        raise ValueError(f"{name} must be a device (cuda) tensor")
+    if device is not None and where != device:
+        raise ValueError(f"{name} is on {t.device}, expected cuda:{device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if device is not None and t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
-        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if dtype is not None:
+        dt = t.dtype
+        if dt is not dtype and (type(dtype) is not tuple or dt not in dtype):
+            raise TypeError(f"{name} must have dtype {dtype}, got {dt}")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
-def _stream_ptr(stream, device) -> ctypes.c_void_p:
+def _device_of(t: torch.Tensor, name: str) -> int:
+    """Device ordinal of the tensor that fixes a call's device; a host tensor
+    is rejected here, before any workspace is taken."""
+    where = t.get_device() if isinstance(t, torch.Tensor) else -1
+    if where < 0:
+        raise ValueError(f"{name} must be a device (cuda) tensor")
+    return where
+
+
+def _stream_ptr(stream, device: int):
+    """Raw hipStream_t of `stream` (a torch stream or a raw handle), else of
+    torch's current stream on `device`."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        return torch._C._cuda_getCurrentRawStream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
 def _workspace(func, nbytes, workspace, stream, device):
@@ -69,7 +89,7 @@ def _workspace(func, nbytes, workspace, stream, device):
         have = workspace.numel() * workspace.element_size()
         if have < nbytes:
             raise ValueError(f"{func}: workspace holds {have} bytes, needs {nbytes}")
-        return ctypes.c_void_p(workspace.data_ptr()), have
+        return workspace.data_ptr(), have
     if nbytes == 0:
         return None, 0
     if stream is not None and not isinstance(stream, torch.cuda.Stream):
@@ -77,7 +97,7 @@ def _workspace(func, nbytes, workspace, stream, device):
     ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
     if stream is not None and stream != torch.cuda.current_stream(device):
         ws.record_stream(stream)  # not reused by torch before the call's work on `stream` ends
-    return ctypes.c_void_p(ws.data_ptr()), nbytes
+    return ws.data_ptr(), nbytes
 
 
 def calibrate_workspace_bytes(shape: RrpShape, n_tokens: int, with_q: bool = True) -> int:
@@ -115,7 +135,7 @@ def _rotate_args(shape, q, k, v, pos, support_b, group, k_codes, k_scales, v_cod
     d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
     T = int(pos.numel())
     dt = k.dtype
-    dev = k.device
+    dev = _device_of(k, "k")
     if n_slots is None:
         n_slots = int(k_codes.shape[0])
     ng = max(1, d // max(1, int(group)))
@@ -188,7 +208,7 @@ def calibrate_angles(shape: RrpShape, q: Optional[torch.Tensor], k: torch.Tensor
     est = ESTIMATORS[estimator] if isinstance(estimator, str) else int(estimator)
     d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
     T = int(pos.numel())
-    dt, dev = k.dtype, k.device
+    dt, dev = k.dtype, _device_of(k, "k")
     ws, ws_bytes = _workspace("rrp_calibrate_angles", calibrate_workspace_bytes(shape, T, q is not None), workspace,
                               stream, dev)
     args = [
@@ -212,7 +232,7 @@ def calibrate_angles_noalloc(shape: RrpShape, q: Optional[torch.Tensor], k: torc
     est = ESTIMATORS[estimator] if isinstance(estimator, str) else int(estimator)
     d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
     T = int(pos.numel())
-    dt, dev = k.dtype, k.device
+    dt, dev = k.dtype, _device_of(k, "k")
     args = [
         ctypes.byref(shape), _dtype_code(k),
         _dev(q, "q", T * hq * d, dt, dev), _dev(k, "k", T * hk * d, dt, dev),
@@ -232,7 +252,7 @@ def quant_error_stats(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, su
     L = _abi.load()
     d, hk = shape.head_dim, shape.n_kv_heads
     T = int(pos.numel())
-    dt, dev = k.dtype, k.device
+    dt, dev = k.dtype, _device_of(k, "k")
     ws, ws_bytes = _workspace("rrp_quant_error_stats", quant_error_stats_workspace_bytes(shape, T), workspace,
                               stream, dev)
     args = [
@@ -263,7 +283,7 @@ def quant_error_sweep(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, gr
     L = _abi.load()
     d, hk = shape.head_dim, shape.n_kv_heads
     T = int(pos.numel())
-    dt, dev = k.dtype, k.device
+    dt, dev = k.dtype, _device_of(k, "k")
     ws, ws_bytes = _workspace("rrp_quant_error_sweep", quant_error_sweep_workspace_bytes(shape, T), workspace,
                               stream, dev)
     args = [
@@ -279,7 +299,7 @@ def quant_error_sweep(shape: RrpShape, k: torch.Tensor, pos: torch.Tensor, *, gr
 def _decode_args(shape, q, k_codes, k_scales, group, seq_start, seq_len, max_len, scores, n_slots, stream):
     d, hq, hk = shape.head_dim, shape.n_q_heads, shape.n_kv_heads
     B = int(seq_len.numel())
-    dev = q.device
+    dev = _device_of(q, "q")
     if n_slots is None:
         n_slots = int(k_codes.shape[0])
     ng = max(1, d // max(1, int(group)))

@@ -49,7 +49,8 @@ struct RotateArgs {
 
 // dtype: 0 fp32, 1 bf16; layout: 0 half-split, 1 interleaved.
 hipError_t launch_rotate_quantize(const RotateArgs& a, int dtype, int head_dim, int layout, hipStream_t st);
-// The small-batch family (0 < n_tokens < 4096), called by launch_rotate_quantize.
+// The small-batch family (n_tokens x row passes per token <= 4096), called by
+// launch_rotate_quantize.
 hipError_t launch_rotate_quantize_split(const RotateArgs& a, int dtype, int head_dim, int layout, hipStream_t st);
 
 }  // namespace rrp

@@ -377,9 +377,10 @@ void rotate_quantize_kernel(const RotateArgs a) {
 }
 
 // Launch one compile-time family: SPLIT = false for large batches (grid-stride
-// over tokens, one wave each), SPLIT = true for small ones (a token's row passes
-// split over up to kSmallBatchWaves / T waves, at most one pass each, so a
-// decode batch is not serialised on one wave per token).
+// over tokens, one wave each), SPLIT = true for small ones (each of a token's
+// row passes on a wave of its own, so a decode batch is not serialised on one
+// wave per token).  The split family takes batches of at most kSmallBatchWaves
+// passes in all.
 constexpr int kSmallBatchWaves = 4096;
 // Grid caps of the large-batch family; past them waves walk several tokens each.
 // Q/K with shared angles: 32K blocks of 4 waves, one token per wave up to 128K
@@ -394,8 +395,10 @@ template <typename E, int D, int LAYOUT, bool SPLIT>
 hipError_t launch_t(const RotateArgs& args, hipStream_t st) {
     RotateArgs a = args;
     const bool ph = a.angle_sets > 1;
-    // Small batches: one wave per block so the work spreads over all CUs.
-    const int wpb = a.n_tokens >= 4096 ? (ph ? kPerSetWaves : 4) : 1;
+    // Small batches (the split family): one wave per block so the work spreads
+    // over all CUs.  One wave per token: blocks of 4 waves at any batch size
+    // (2048 tokens at d 64 took 11.8 us with 1-wave blocks, 7.8 us with 4).
+    const int wpb = SPLIT ? 1 : (ph ? kPerSetWaves : 4);
     a.split = 1;
     if constexpr (SPLIT) {
         constexpr int R = Geo<E, D>::R;

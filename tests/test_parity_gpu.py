@@ -695,14 +695,25 @@ def test_per_head_fp32_inputs_and_layouts(layout, b):
     print(layout, b, check_rotate(w, sub, out, ang, b, 16, np.arange(T), layout=layout, ah=w.n_kv_heads))
 
 
+def split_bound(w, with_v=False, with_q=True):
+    """Largest batch the split-pass kernel family takes: the library runs a
+    batch there when its tokens x row passes per token are at most 4096 (one
+    wave per pass), else one wave per token with a grid stride.  A pass is
+    2048 / (head_dim x element bytes) rows of one token."""
+    rows = 2048 // (w.head_dim * (4 if w.dtype == "f32" else 2))
+    npass = (-(-w.n_q_heads // rows) if with_q else 0) + (2 if with_v else 1) * -(-w.n_kv_heads // rows)
+    return 4096 // npass
+
+
 @pytest.mark.parametrize("ah,with_v", [(0, False), (0, True), (8, False)])
 def test_small_batch_split_matches_grid_stride_kernel(ah, with_v):
-    """Batches under 4096 tokens run the split-pass kernel family, larger ones the
+    """Small batches run the split-pass kernel family, larger ones the
     grid-stride family: the same tokens give the same bits either way."""
     w = W.WORKLOADS[3]
     big = vinputs(3, 4096) if with_v else W.make_inputs(3, n_tokens=4096)
-    small = {k: (v[:4095] if isinstance(v, np.ndarray) else v) for k, v in big.items()}
-    small["n_slots"] = 4095
+    T = split_bound(w, with_v)
+    small = {k: (v[:T] if isinstance(v, np.ndarray) else v) for k, v in big.items()}
+    small["n_slots"] = T
     ang = random_angle_sets(w, 1500) if ah else random_angles(w.n_pairs, 1500)
     run = (lambda inp: run_rotate_qkv(w, inp, ang, 128, 32, ah=ah)) if with_v else \
         (lambda inp: run_rotate(w, inp, ang, 128, 32, ah=ah))
@@ -711,10 +722,27 @@ def test_small_batch_split_matches_grid_stride_kernel(ah, with_v):
     if with_v:
         keys += ["v_codes", "v_scales", "v_rot_f32", "v_scale_f32"]
     for key in keys:
-        x, y = a[key][:4095], c[key]
+        x, y = a[key][:T], c[key]
         if x.dtype == torch.bfloat16:
             x, y = x.view(torch.int16), y.view(torch.int16)
         assert torch.equal(x, y), key
+
+
+@pytest.mark.parametrize("n,b,g,ah,with_v", [(2, 16, 16, 0, False), (2, 64, 8, 0, True), (3, 128, 32, 0, False),
+                                            (3, 2, 2, 8, False), (3, 64, 128, 0, True), (1, 64, 4, 0, False)])
+def test_rotate_parity_at_the_kernel_family_bound(n, b, g, ah, with_v):
+    """The last batch size the split-pass family takes and the first one the
+    grid-stride family takes, every token against the oracle."""
+    w = W.WORKLOADS[n]
+    bound = split_bound(w, with_v)
+    for T in (bound, bound + 1):
+        inp = W.make_inputs(n, n_tokens=T, want_v=with_v)
+        ang = random_angle_sets(w, 1900 + T) if ah else random_angles(w.n_pairs, 1900 + T)
+        out = run_rotate_qkv(w, inp, ang, b, g, ah=ah) if with_v else run_rotate(w, inp, ang, b, g, ah=ah)
+        rep = check_rotate(w, inp, out, ang, b, g, np.arange(T), ah=ah)
+        if with_v:
+            rep["v"] = check_v(w, inp, out, g, np.arange(T))
+        print(f"workload {n} T={T} b={b} g={g} sets={max(ah, 1)} v={with_v}: {rep}")
 
 
 def test_per_head_in_place_and_k_only():

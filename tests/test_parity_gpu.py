@@ -8,6 +8,8 @@ sample of tokens that the oracle evaluates one by one.  Tolerances: see
 oracle/compare.py.
 """
 import math
+import os
+import re
 
 import numpy as np
 import pytest
@@ -695,14 +697,23 @@ def test_per_head_fp32_inputs_and_layouts(layout, b):
     print(layout, b, check_rotate(w, sub, out, ang, b, 16, np.arange(T), layout=layout, ah=w.n_kv_heads))
 
 
+def small_batch_waves():
+    """The library's bound on the split-pass family (kSmallBatchWaves), read
+    from the kernel source so the tests at the bound follow it."""
+    src = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "rotation_rope_pair_amd", "csrc",
+                       "rrp_rotate_kernel.hpp")
+    with open(src) as f:
+        return int(re.search(r"constexpr int kSmallBatchWaves = (\d+);", f.read()).group(1))
+
+
 def split_bound(w, with_v=False, with_q=True):
     """Largest batch the split-pass kernel family takes: the library runs a
-    batch there when its tokens x row passes per token are at most 4096 (one
-    wave per pass), else one wave per token with a grid stride.  A pass is
-    2048 / (head_dim x element bytes) rows of one token."""
+    batch there when its tokens x row passes per token are at most
+    kSmallBatchWaves (one wave per pass), else one wave per token with a grid
+    stride.  A pass is 2048 / (head_dim x element bytes) rows of one token."""
     rows = 2048 // (w.head_dim * (4 if w.dtype == "f32" else 2))
     npass = (-(-w.n_q_heads // rows) if with_q else 0) + (2 if with_v else 1) * -(-w.n_kv_heads // rows)
-    return 4096 // npass
+    return small_batch_waves() // npass
 
 
 @pytest.mark.parametrize("ah,with_v", [(0, False), (0, True), (8, False)])
